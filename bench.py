@@ -1,0 +1,216 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the Wan-14B-shaped
+720p workload (grid 21x45x80 = 75600 tokens, B=1, 40 heads of 128, bf16):
+  1. self-attention forward with 3D RoPE  (keys pre-rotated, queries rotated on load; O, LSE)
+  2. text cross-attention forward         (75600 video tokens x 512 text tokens, valid length ~U[20,512])
+  3. self-attention backward              (dQ, dK, dV incl. the RoPE gradient)
+Inputs are synthetic (seeded N(0,1) in bf16) and resident in HBM before timing.
+
+The reported metric is the self-attention forward's throughput: algorithmic
+4*B*H*L^2*D flop divided by the forward's mean duration, measured with HIP
+events on the stream the library launches on, inside the timed steps.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain device copy of known size (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, w, rope, scale):
+    """The fp64 oracle on a bounded sample: 64 seeded query rows of every head."""
+    import numpy as np
+    import oracle
+    import synth
+    rows = inp["rows"]
+    t0 = time.perf_counter()
+    for h in range(w.H):
+        sl = (slice(0, 1), slice(None), slice(h, h + 1))
+        oracle.self_fwd_ref(synth.bf16_bits_to_f64(inp["q"][sl]), synth.bf16_bits_to_f64(inp["k"][sl]),
+                            synth.bf16_bits_to_f64(inp["v"][sl]), scale, w.grid, rope, rows=rows[:, h:h + 1])
+    dt = time.perf_counter() - t0
+    n_rows = rows.shape[1] * rows.shape[2]
+    flop = 4.0 * n_rows * w.L * w.D
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"self-attention forward (fp64 NumPy, 3D RoPE) of {rows.shape[2]} seeded query rows "
+                      f"x {w.H} heads against all {w.L} keys of the 720p workload; {dt:.2f} s",
+            "seconds": dt, "flop": flop}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the heads or key blocks would shard across GPUs; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import spatio_temporal_attention_amd as wa
+    import synth
+
+    if not os.path.exists(wa.LIB_PATH):
+        from spatio_temporal_attention_amd import build
+        build.build()
+    wa.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    w = synth.WORKLOADS[4]
+    B, L, H, D = w.B, w.L, w.H, w.D
+    rope = wa.RopeConfig(48, 40, 40, 10000.0)
+    scale = 1.0 / math.sqrt(D)
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(4)
+    ctx = synth.make_text_context(4, B, H)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (dev_bf16(inp[n]) for n in ("q", "k", "v", "dout"))
+    tk, tv = dev_bf16(ctx["k"]), dev_bf16(ctx["v"])
+    k_lens = torch.from_numpy(ctx["k_lens"]).to(dev)
+    table = wa.rope_table(w.grid, rope, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    xo = torch.empty_like(q)
+    xlse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws_f = torch.empty(wa.self_fwd_workspace_bytes(B, L, H, D, True), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(wa.self_bwd_workspace_bytes(B, L, H, D, True), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wa.self_fwd(q, k, v, grid=w.grid, table=table, rope=rope, scale=scale, out=o, lse=lse, workspace=ws_f)
+        if ev is not None:
+            ev[1].record()
+        if args.fwd_only:
+            return
+        wa.cross_fwd(q, tk, tv, k_lens, scale=scale, out=xo, lse=xlse)
+        if ev is not None:
+            ev[2].record()
+        wa.self_bwd(q, k, v, o, lse, do, grid=w.grid, table=table, rope=rope, scale=scale, workspace=ws_b,
+                    dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    if not args.fwd_only:
+        cross_ms = [e[1].elapsed_time(e[2]) for e in events]
+        bwd_ms = [e[2].elapsed_time(e[3]) for e in events]
+    log(f"timed {args.steps} steps in {elapsed:.2f} s; forward ms: {[round(x, 2) for x in fwd_ms]}")
+
+    fwd_flop = 4.0 * B * H * L * L * D
+    fwd_mean = sum(fwd_ms) / len(fwd_ms)
+    fwd_tflops = fwd_flop / (fwd_mean * 1e-3) / 1e12
+    extra = {}
+    if not args.fwd_only:
+        kl = ctx["k_lens"].astype(np.int64)
+        cross_flop = 4.0 * H * D * L * float(kl.sum())
+        cross_bytes = 2.0 * (B * L * H * D * 2) + float(kl.sum()) * H * D * 4 + B * H * L * 4
+        bwd_flop = 8.0 * B * H * L * L * D
+        cross_mean = sum(cross_ms) / len(cross_ms)
+        bwd_mean = sum(bwd_ms) / len(bwd_ms)
+        extra = {
+            "fwd_ms": round(fwd_mean, 3),
+            "bwd_ms": round(bwd_mean, 3),
+            "bwd_tflops": round(bwd_flop / (bwd_mean * 1e-3) / 1e12, 1),
+            "cross_ms": round(cross_mean, 4),
+            "cross_tflops": round(cross_flop / (cross_mean * 1e-3) / 1e12, 2),
+            "cross_gbs": round(cross_bytes / (cross_mean * 1e-3) / 1e9, 1),
+            "cross_k_lens": [int(x) for x in kl],
+        }
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    result = {
+        "metric": "self-attn fwd TFLOP/s + % bf16 MFMA peak, L=75600 H=40 D=128 (14B 720p)",
+        "value": round(fwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16; no dataset or weights involved)",
+        "config": {"workload": "wan14b-720p self-attn fwd+bwd + text cross-attn",
+                   "grid": list(w.grid), "B": B, "L": L, "H": H, "D": D, "rope_split": [48, 40, 40],
+                   "rope_theta": 10000.0, "text_tokens": 512, "parallelism": "none (1 GPU)",
+                   "step": "self_fwd + cross_fwd + self_bwd" if not args.fwd_only else "self_fwd"},
+        "pct_bf16_peak": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel (+ key pre-rotation inside the same timed call)",
+                     "flop_per_launch": fwd_flop},
+    }
+    result.update(extra)
+    if not args.no_cpu_baseline:
+        log("running the CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(inp, w, rope, scale)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * wanattn -- spatio-temporal attention with 3D RoPE for Wan-style video DiTs,
+ * on AMD Instinct MI355X (gfx950).  Plain C interface.
+ *
+ * Sources (page title, section):
+ *   [notes]  "Wan -- Open and Advanced Large-Scale Video Generative Models (Wan2.1)"
+ *            reading notes (gojay.top): "2. Model Design" (Wan-VAE paragraph:
+ *            latent grid [1+T/4, H/8, W/8]; DiT backbone paragraph: (1,2,2)
+ *            patch, L = (1+T/4)*H/16*W/16; DiT block paragraph: 3D RoPE on the
+ *            code side), the code-notes config table ("1.3B vs 14B": dim
+ *            1536/5120, 12/40 heads, so head dim 128; umT5 with 512 tokens),
+ *            "3. Training" (bf16).
+ *   [lit619] "Wan Team, Alibaba (2025) -- ARXIV-2503.20314", "Key takeaways":
+ *            full spatio-temporal self-attention over latent patches plus
+ *            cross-attention to umT5 text embeddings (Backbone); attention
+ *            dominates at long sequence lengths and is split across GPUs by
+ *            Ring (outside) x Ulysses (inside) context parallelism.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Tensors.  q, k, v, o, dout, dq, dk, dv are contiguous [B, L, H, D] bf16
+ *    (D innermost; passed as void*).  lse is contiguous [B, H, L] fp32, the
+ *    natural-log log-sum-exp of each query row's scaled scores.  Cross-attention
+ *    uses [B, Lq, H, D] for q/o and [B, Lk, H, D] for k/v.  D must be 128.
+ *  Tokens and positions.  Token n of a self-attention sequence sits at grid
+ *    position (f, h, w) = (n / (gh*gw), (n / gw) % gh, n % gw): row-major over
+ *    the post-patchify grid wanattn_grid {f, h, w}, so f*h*w == L.
+ *  3D RoPE.  The head dim splits into a time segment [0, d_f), a height
+ *    segment [d_f, d_f+d_h) and a width segment [d_f+d_h, D).  Pair j of a
+ *    segment of width d_a (elements o_a+2j, o_a+2j+1) turns by the angle
+ *    p_a * theta^(-2j/d_a), p_a being the token's position on that axis:
+ *      y[2j]   = x[2j] cos - x[2j+1] sin,   y[2j+1] = x[2j] sin + x[2j+1] cos.
+ *    Each width must be even and >= 0, d_f + d_h + d_w == D, theta > 0.
+ *  Rounding.  All arithmetic is fp32 (MFMA accumulates bf16 products in fp32);
+ *    every fp32 -> bf16 rounding is round-to-nearest-even.  Rotated q/k are
+ *    rounded to bf16 before the score products.
+ *  Memory.  Every pointer is device memory owned by the caller, which keeps it
+ *    alive until the stream's work has finished.  bf16 buffers, the rope table
+ *    and workspaces must be 16-byte aligned; fp32 and int32 buffers 4-byte
+ *    aligned.  Outputs must not alias inputs (except x == y in wanattn_rope3d).
+ *    The library allocates no device memory, keeps no global state, never
+ *    synchronizes and never prints.
+ *  Streams.  `stream` is a hipStream_t (NULL: the default stream).  All work
+ *    is enqueued asynchronously on it; calls from several host threads on
+ *    different streams are safe.
+ *  Errors.  Arguments are validated on the host before anything is enqueued;
+ *    on failure the call returns a nonzero WANATTN_ERR_* code and touches no
+ *    memory.  WANATTN_ERR_HIP reports a launch failure (hipGetLastError).
+ *    Faults inside kernels surface at the caller's next stream synchronization.
+ */
+#ifndef WANATTN_H
+#define WANATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WANATTN_HEAD_DIM 128
+
+enum wanattn_status {
+  WANATTN_OK = 0,
+  WANATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+  WANATTN_ERR_SHAPE = 2,        /* a size is <= 0 or too large, or f*h*w != L */
+  WANATTN_ERR_UNSUPPORTED = 3,  /* D != 128, bad rotary split or theta, non-finite scale */
+  WANATTN_ERR_ALIGN = 4,        /* a buffer is not aligned as documented above */
+  WANATTN_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the *_workspace_bytes value */
+  WANATTN_ERR_HIP = 6           /* the HIP runtime rejected a launch */
+};
+
+/* Post-patchify token grid (frames, rows, columns): [1+T/4, H/16, W/16] for a
+ * 1+T frame H x W clip ([notes] 2. Model Design). */
+typedef struct wanattn_grid {
+  int32_t f, h, w;
+} wanattn_grid;
+
+/* Head-dim split between the time/height/width axes and the rotary base
+ * (the pages name 3D RoPE without its constants; the workloads use 48/40/40
+ * and theta = 10000). */
+typedef struct wanattn_rope {
+  int32_t d_f, d_h, d_w;
+  float theta;
+} wanattn_rope;
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* wanattn_strerror(int status);
+
+/* ---------------------------------------------------------------------------
+ * 3D RoPE table ([notes] 2. Model Design, DiT block paragraph: 3D RoPE over
+ * time, height, width).
+ *
+ * Layout: three consecutive blocks, time then height then width.  Block a
+ * holds size_a * (d_a/2) entries; entry (p, j) of block a is the float pair
+ * (cos, sin) of p * theta^(-2j/d_a), computed in fp64 and rounded to fp32.
+ * wanattn_rope_table_bytes returns 8 * (f*d_f/2 + h*d_h/2 + w*d_w/2), or 0 if
+ * the grid or split is invalid.
+ * ------------------------------------------------------------------------- */
+size_t wanattn_rope_table_bytes(wanattn_grid g, wanattn_rope r);
+
+/* Fill `table` (device, wanattn_rope_table_bytes(g, r) bytes) on `stream`. */
+int wanattn_rope_table_init(float* table, wanattn_grid g, wanattn_rope r, void* stream);
+
+/* y = R(p) x for every token (inverse != 0: y = R(p)^T x, the rotation by
+ * minus the angle).  x, y: [B, L, H, D] bf16; x == y is allowed (in place).
+ * Requires g.f*g.h*g.w == L and a table built for (g, r). */
+int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D,
+                   wanattn_grid g, wanattn_rope r, const float* table,
+                   int inverse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Self-attention forward: full (non-causal) softmax attention of every token
+ * over every token of the same sequence and head ([lit619] Key takeaways,
+ * Backbone; [notes] 1. Introduction), with 3D RoPE on q and k:
+ *   s_ij = scale * <R(p_i) q_i, R(p_j) k_j>,  LSE_i = ln sum_j exp(s_ij),
+ *   O_i  = sum_j exp(s_ij - LSE_i) v_j.
+ * table == NULL: no rotation (g and r are then ignored).
+ * lse may be NULL (not written).  scale: any finite value (1/sqrt(D) usual).
+ * Workspace: with a table, ws must hold wanattn_self_fwd_workspace_bytes bytes
+ * (the rotated keys, bf16 [B, L, H, D]); without one it is unused (may be NULL).
+ * ------------------------------------------------------------------------- */
+size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
+
+int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int L, int H, int D,
+                     wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Self-attention backward (training, [notes] 3. Training: bf16; the formulas
+ * are the calculus of the forward above).  Given o and lse from
+ * wanattn_self_fwd and the output gradient dout:
+ *   Delta_i = <dout_i, o_i>;  P_ij = exp(s_ij - LSE_i);  dV_j = sum_i P_ij dout_i;
+ *   dS_ij = P_ij (<dout_i, v_j> - Delta_i);
+ *   dq_i = R(p_i)^T scale sum_j dS_ij R(p_j) k_j;  dk_j = R(p_j)^T scale sum_i dS_ij R(p_i) q_i.
+ * Gradients are with respect to the unrotated q and k.  table == NULL: no RoPE.
+ * Workspace: wanattn_self_bwd_workspace_bytes bytes (Delta fp32 [B, H, L], and
+ * with a table the rotated q and k, bf16 [B, L, H, D] each).
+ * ------------------------------------------------------------------------- */
+size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
+
+int wanattn_self_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv,
+                     int B, int L, int H, int D,
+                     wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Cross-attention forward: video-token queries over text-token keys and values
+ * ([lit619] Key takeaways, Backbone: cross-attention to umT5 embeddings;
+ * [notes] config table: 512 text tokens).  No RoPE.  Keys j >= k_lens[b] are
+ * padding: they are excluded and never read (their contents may be anything,
+ * NaN included).  k_lens: device int32 [B], each clamped to [0, Lk]; NULL
+ * means every key is valid.  A row with no valid key gets O = 0 and
+ * LSE = -inf.  lse may be NULL.
+ * ------------------------------------------------------------------------- */
+int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens,
+                      void* o, float* lse,
+                      int B, int Lq, int Lk, int H, int D, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WANATTN_H */

@@ -1,0 +1,177 @@
+// The exported C interface of libwanattn (declared in include/wanattn.h):
+// argument validation on the host, then launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "../../include/wanattn.h"
+#include "kernels.h"
+#include "validate.h"
+
+#define WANATTN_API extern "C" __attribute__((visibility("default")))
+
+namespace wanattn {
+namespace {
+
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+RopeDev make_rope(wanattn_grid g, wanattn_rope r, const float* table) {
+  RopeDev d{};
+  d.table = reinterpret_cast<const float2*>(table);
+  if (table != nullptr) {
+    d.gh = g.h;
+    d.gw = g.w;
+    d.nf = r.d_f / 2;
+    d.nh = r.d_h / 2;
+    d.nw = r.d_w / 2;
+    d.off_h = g.f * d.nf;
+    d.off_w = d.off_h + g.h * d.nh;
+  } else {
+    d.gh = 1;
+    d.gw = 1;
+  }
+  return d;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? WANATTN_OK : WANATTN_ERR_HIP; }
+
+}  // namespace
+}  // namespace wanattn
+
+using namespace wanattn;
+
+WANATTN_API const char* wanattn_strerror(int status) {
+  switch (status) {
+    case WANATTN_OK: return "wanattn: success";
+    case WANATTN_ERR_NULL: return "wanattn: a required pointer is NULL";
+    case WANATTN_ERR_SHAPE: return "wanattn: invalid shape (size <= 0, too large, or grid f*h*w != L)";
+    case WANATTN_ERR_UNSUPPORTED:
+      return "wanattn: unsupported argument (head dim must be 128; rotary split must be even widths summing to "
+             "128; theta > 0; finite scale)";
+    case WANATTN_ERR_ALIGN: return "wanattn: misaligned buffer (bf16/table/workspace need 16 bytes, fp32/int32 4)";
+    case WANATTN_ERR_WORKSPACE: return "wanattn: workspace missing or too small";
+    case WANATTN_ERR_HIP: return "wanattn: HIP launch failed";
+    default: return "wanattn: unknown status";
+  }
+}
+
+WANATTN_API size_t wanattn_rope_table_bytes(wanattn_grid g, wanattn_rope r) {
+  const int64_t n = rope_table_entries(g, r);
+  return n < 0 ? 0 : (size_t)n * 2 * sizeof(float);
+}
+
+WANATTN_API int wanattn_rope_table_init(float* table, wanattn_grid g, wanattn_rope r, void* stream) {
+  if (table == nullptr) return WANATTN_ERR_NULL;
+  if (rope_table_entries(g, r) < 0) return WANATTN_ERR_SHAPE;
+  if (!aligned(table, 16)) return WANATTN_ERR_ALIGN;
+  return hip_status(launch_rope_table(table, g.f, g.h, g.w, r.d_f, r.d_h, r.d_w, (double)r.theta,
+                                      (hipStream_t)stream));
+}
+
+WANATTN_API int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
+                               const float* table, int inverse, void* stream) {
+  const int rc = validate_rope3d(x, y, B, L, H, D, g, r, table);
+  if (rc != WANATTN_OK) return rc;
+  return hip_status(launch_rope3d((const uint16_t*)x, (uint16_t*)y, B, L, H, make_rope(g, r, table), inverse != 0,
+                                  (hipStream_t)stream));
+}
+
+WANATTN_API size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope) {
+  return self_fwd_ws_bytes(B, L, H, D, with_rope);
+}
+
+WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
+                                 int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  const int rc = validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  const hipStream_t s = (hipStream_t)stream;
+  const RopeDev rope = make_rope(g, r, table);
+  const uint16_t* keys = (const uint16_t*)k;
+  if (table != nullptr) {
+    // Keys are rotated once into the workspace (one HBM pass) instead of on
+    // every (query tile, key tile) visit; queries are rotated on their load.
+    uint16_t* kr = (uint16_t*)ws;
+    const int e = hip_status(launch_rope3d(keys, kr, B, L, H, rope, false, s));
+    if (e != WANATTN_OK) return e;
+    keys = kr;
+  }
+  FwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = keys;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.k_lens = nullptr;
+  p.rope = rope;
+  p.B = B;
+  p.Lq = L;
+  p.Lk = L;
+  p.H = H;
+  p.scale_log2 = scale * LOG2E_F;
+  return hip_status(launch_attn_fwd(p, s));
+}
+
+WANATTN_API size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope) {
+  return self_bwd_ws_bytes(B, L, H, D, with_rope);
+}
+
+WANATTN_API int wanattn_self_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, int B, int L, int H, int D,
+                                 wanattn_grid g, wanattn_rope r, const float* table, float scale, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  const int rc = validate_self_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, L, H, D, g, r, table, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  const hipStream_t s = (hipStream_t)stream;
+  BwdParams p{};
+  const size_t delta_bytes = ((size_t)B * H * L * 4 + 255) & ~(size_t)255;
+  p.delta = (float*)ws;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.rope = make_rope(g, r, table);
+  if (table != nullptr) {
+    uint16_t* qr = (uint16_t*)((char*)ws + delta_bytes);
+    uint16_t* kr = qr + (size_t)B * L * H * D;
+    int e = hip_status(launch_rope3d((const uint16_t*)q, qr, B, L, H, p.rope, false, s));
+    if (e != WANATTN_OK) return e;
+    e = hip_status(launch_rope3d((const uint16_t*)k, kr, B, L, H, p.rope, false, s));
+    if (e != WANATTN_OK) return e;
+    p.q = qr;
+    p.k = kr;
+  }
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.B = B;
+  p.L = L;
+  p.H = H;
+  p.scale = scale;
+  p.scale_log2 = scale * LOG2E_F;
+  int e = hip_status(launch_bwd_delta(p, s));
+  if (e != WANATTN_OK) return e;
+  e = hip_status(launch_bwd_dkdv(p, s));
+  if (e != WANATTN_OK) return e;
+  return hip_status(launch_bwd_dq(p, s));
+}
+
+WANATTN_API int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, void* o,
+                                  float* lse, int B, int Lq, int Lk, int H, int D, float scale, void* stream) {
+  const int rc = validate_cross_fwd(q, k, v, k_lens, o, lse, B, Lq, Lk, H, D, scale);
+  if (rc != WANATTN_OK) return rc;
+  FwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.k_lens = k_lens;
+  p.rope = make_rope(wanattn_grid{1, 1, 1}, wanattn_rope{0, 0, 0, 1.f}, nullptr);
+  p.B = B;
+  p.Lq = Lq;
+  p.Lk = Lk;
+  p.H = H;
+  p.scale_log2 = scale * LOG2E_F;
+  return hip_status(launch_attn_fwd(p, (hipStream_t)stream));
+}

@@ -1,0 +1,222 @@
+// Attention forward for gfx950: full self-attention with 3D RoPE on the query
+// load (keys arrive already rotated), and masked cross-attention, sharing one
+// kernel.
+//
+// Computes, per (batch b, head h, query i), over the valid keys j < n_keys:
+//   s_ij = scale <q~_i, k~_j>,  O_i = sum_j softmax_j(s_ij) v_j,  LSE_i = ln sum_j exp(s_ij)
+// -- full spatio-temporal attention over latent patches ("Wan Team, Alibaba
+// (2025)", Key takeaways, Backbone) with positions entering through 3D RoPE
+// (Wan2.1 reading notes, 2. Model Design, DiT block paragraph).
+//
+// Design (one workgroup = 4 waves = 128 query rows of one (b, h)):
+//  * each wave keeps its 32 rotated query rows in registers as the B operand
+//    of S^T = K Q^T (bf16 MFMA 32x32x16), so every lane owns one query row and
+//    the softmax needs one cross-lane step (lane l <-> l^32) per tile;
+//  * K and V tiles of 64 keys are staged through LDS (row-major, swizzled),
+//    double-buffered: the next tile's global loads are in flight while the
+//    current one is multiplied;
+//  * O^T += V^T P^T reads V through the LDS transpose read and takes P
+//    straight from the S^T accumulator registers (bf16, RNE);
+//  * online softmax in fp32 in the log2 domain (scale * log2 e folded in);
+//  * workgroups are ordered head-major and XCD-aware so that the resident
+//    workgroups of one XCD walk the same head's K/V through its L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace wanattn {
+
+namespace {
+
+constexpr int FWD_WAVES = 4;
+constexpr int FWD_BR = 32 * FWD_WAVES;   // query rows per workgroup
+constexpr int FWD_BC = TILE_ROWS;         // keys per tile
+
+template <bool POS_SCALE>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE_ELEMS];   // [buffer][K|V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;       // which 32-lane half
+  const int col = lane & 31;        // query row of this lane within the wave
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = logical % p.n_qtiles;
+  const int bh = logical / p.n_qtiles;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+
+  int n_keys = p.Lk;
+  if (p.k_lens != nullptr) n_keys = min(max(p.k_lens[b], 0), p.Lk);
+
+  const int64_t q_row_stride = (int64_t)p.H * HD;
+  const uint16_t* qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * HD;
+  const uint16_t* kbase = p.k + ((int64_t)b * p.Lk * p.H + h) * HD;
+  const uint16_t* vbase = p.v + ((int64_t)b * p.Lk * p.H + h) * HD;
+
+  // ---- query fragments (B operand of S^T = K Q^T): lane holds row i, d in [16s + 8*half, +8)
+  const int i = qt * FWD_BR + wave * 32 + col;
+  const bool row_ok = i < p.Lq;
+  bf16x8 qf[8];
+  {
+    TokenPos pos{0, 0, 0};
+    if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      const int c = 2 * s + half;
+      if (row_ok) {
+        x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
+        if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 o_acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o_acc[d] = f32x16{};
+  float m_run = -INFINITY;   // running max of scale*log2e*s (this lane's row)
+  float l_run = 0.f;         // this lane's partial exp-sum (the other half holds the rest)
+  const float c2 = p.scale_log2;
+
+  const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
+
+  if (n_tiles > 0) {
+    TileRegs kr, vr;
+    tile_load(kr, kbase, q_row_stride, 0, n_keys, tid);
+    tile_load(vr, vbase, q_row_stride, 0, n_keys, tid);
+    tile_store(smem[0][0], kr, tid);
+    tile_store(smem[0][1], vr, tid);
+    __syncthreads();
+
+    for (int t = 0; t < n_tiles; ++t) {
+      const int buf = t & 1;
+      const bool has_next = t + 1 < n_tiles;
+      if (has_next) {
+        tile_load(kr, kbase, q_row_stride, (t + 1) * FWD_BC, n_keys, tid);
+        tile_load(vr, vbase, q_row_stride, (t + 1) * FWD_BC, n_keys, tid);
+      }
+      const uint16_t* ks = smem[buf][0];
+      const uint16_t* vs = smem[buf][1];
+
+      // S^T (64 keys x 32 queries) as two 32x32 blocks.
+      f32x16 s_acc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s_acc[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
+          s_acc[kb] = mfma32(a, qf[s], s_acc[kb]);
+        }
+      }
+
+      // Scores in the log2 domain; keys past n_keys get -inf.
+      float sv[2][16];
+      const int key0 = t * FWD_BC;
+      const bool partial = key0 + FWD_BC > n_keys;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float x;
+          if (POS_SCALE) x = s_acc[kb][j];
+          else x = s_acc[kb][j] * c2;
+          if (partial) {
+            const int key = key0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (key >= n_keys) x = -INFINITY;
+          }
+          sv[kb][j] = x;
+        }
+      }
+      float mx = sv[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
+      mx = xor32_max(mx);
+      if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+
+      float psum = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float e;
+          if (POS_SCALE) e = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_new));
+          else e = __builtin_amdgcn_exp2f(sv[kb][j] - m_new);
+          pv[j] = e;
+          psum += e;
+        }
+        pf[2 * kb] = pack_acc8(pv);
+        pf[2 * kb + 1] = pack_acc8(pv + 8);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
+
+      // O^T (128 d x 32 queries) += V^T P^T over the 4 groups of 16 keys.
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+          const bf16x8 a = lds_col_frag(vs, kg * 16, d * 32, lane);
+          o_acc[d] = mfma32(a, pf[kg], o_acc[d]);
+        }
+      }
+
+      if (has_next) {
+        tile_store(smem[buf ^ 1][0], kr, tid);
+        tile_store(smem[buf ^ 1][1], vr, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: O = O / l (bf16), LSE = ln sum exp(s) = ln2 * (m + log2 l)
+  const float l_tot = xor32_sum(l_run);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    uint16_t* orow = p.o + ((int64_t)b * p.Lq * p.H + h) * HD + (int64_t)i * q_row_stride;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        u32x2 w;
+        w[0] = pack_bf16(o_acc[d][4 * jq] * inv, o_acc[d][4 * jq + 1] * inv);
+        w[1] = pack_bf16(o_acc[d][4 * jq + 2] * inv, o_acc[d][4 * jq + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d * 32 + 8 * jq + 4 * half) = w;
+      }
+    }
+    if (p.lse != nullptr && half == 0) {
+      const float lse = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+                                      : -INFINITY;
+      p.lse[((int64_t)b * p.H + h) * p.Lq + i] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
+  FwdParams q = p;
+  q.n_qtiles = (p.Lq + FWD_BR - 1) / FWD_BR;
+  const int64_t total = (int64_t)q.n_qtiles * p.H * p.B;
+  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)total), block(256);
+  if (p.scale_log2 > 0.f) {
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, block, 0, stream, q);
+  } else {
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, block, 0, stream, q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wanattn

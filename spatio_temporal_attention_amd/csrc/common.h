@@ -1,0 +1,228 @@
+// Device-side building blocks shared by the wanattn kernels (gfx950 / CDNA4).
+//
+// * bf16 <-> fp32 helpers (fp32 -> bf16 is round-to-nearest-even via v_cvt_pk_bf16_f32)
+// * the 3D RoPE rotation of one (even, odd) element pair
+// * staging of 64-row x 128-column bf16 tiles into LDS in a row-major layout
+//   whose 16-byte chunks are XOR-swizzled per row, read back either as
+//   16-byte row fragments (MFMA operands whose k index runs along the row) or
+//   through the LDS transpose read (operands whose k index runs down a column)
+// * MFMA 32x32x16 bf16 wrappers and their register layouts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wanattn {
+
+constexpr int HD = 128;               // head dim (the only one supported)
+constexpr int TILE_ROWS = 64;         // rows of one staged tile
+constexpr int TILE_ELEMS = TILE_ROWS * HD;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 p = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// ---------------------------------------------------------------------------
+// 3D RoPE.  The table holds (cos, sin) float pairs: time block [f][d_f/2],
+// then height block [h][d_h/2], then width block [w][d_w/2].
+// ---------------------------------------------------------------------------
+struct RopeDev {
+  const float2* table;  // nullptr: no rotation
+  int gh, gw;           // grid rows and columns (token n -> f = n/(gh*gw), h = (n/gw)%gh, w = n%gw)
+  int nf, nh, nw;       // pairs per segment: d_f/2, d_h/2, d_w/2
+  int off_h, off_w;     // first table entry of the height and width blocks
+};
+
+struct TokenPos { int f, h, w; };
+
+__device__ __forceinline__ TokenPos token_pos(const RopeDev& r, int n) {
+  const int hw = r.gh * r.gw;
+  TokenPos p;
+  p.f = n / hw;
+  const int rem = n - p.f * hw;
+  p.h = rem / r.gw;
+  p.w = rem - p.h * r.gw;
+  return p;
+}
+
+// (cos, sin) of pair k (0 <= k < 64) of a token at position p.
+__device__ __forceinline__ float2 rope_cs(const RopeDev& r, const TokenPos& p, int k) {
+  int idx;
+  if (k < r.nf) idx = p.f * r.nf + k;
+  else if (k < r.nf + r.nh) idx = r.off_h + p.h * r.nh + (k - r.nf);
+  else idx = r.off_w + p.w * r.nw + (k - r.nf - r.nh);
+  return r.table[idx];
+}
+
+// Rotate (x0, x1) by the angle whose (cos, sin) is cs; inverse uses minus the angle.
+// Written with explicit fmaf so every kernel rounds identically.
+__device__ __forceinline__ void rope_rotate(float& x0, float& x1, float2 cs, bool inverse) {
+  const float s = inverse ? -cs.y : cs.y;
+  const float y0 = fmaf(x0, cs.x, -(x1 * s));
+  const float y1 = fmaf(x0, s, x1 * cs.x);
+  x0 = y0;
+  x1 = y1;
+}
+
+// Rotate the 8 bf16 elements of a 16-byte chunk holding head-dim elements
+// [8c, 8c+8) (pairs 4c .. 4c+3) of a token at position p; result rounded to bf16.
+__device__ __forceinline__ u32x4 rope_chunk(const RopeDev& r, const TokenPos& p, int c, u32x4 x, bool inverse) {
+  u32x4 y;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float x0 = bf16_lo(x[t]);
+    float x1 = bf16_hi(x[t]);
+    rope_rotate(x0, x1, rope_cs(r, p, 4 * c + t), inverse);
+    y[t] = pack_bf16(x0, x1);
+  }
+  return y;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles: 64 rows x 128 bf16, row-major, 256 bytes per row, no padding.
+// The 16 chunks (16 bytes each) of row r are stored at chunk c ^ swz(r).
+// swz permutes 0..15 so that (a) 8 consecutive rows read at one logical chunk
+// hit 8 distinct bank groups (16-byte row fragments), and (b) the 4 rows x
+// 32 bytes read by each 16-lane group of a transpose read do as well.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) {
+  return (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8)) & 15;
+}
+
+// Offset (in bf16 elements) of element (row, col) inside a tile; col % 8 kept.
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+}
+
+// Global -> register staging of a 64-row tile: thread t (of 256) owns rows
+// 4*(t/16) + i, i = 0..3, at 16-byte column chunk t%16.  Each 16-lane group of
+// a load instruction reads one whole 256-byte row (coalesced).  Rows >= nrows
+// are zero and never read from memory.
+struct TileRegs {
+  u32x4 r[4];
+};
+
+__device__ __forceinline__ void tile_load(TileRegs& t, const uint16_t* base, int64_t row_stride,
+                                          int row0, int nrows, int tid) {
+  const int c = tid & 15;
+  const int rq = (tid >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rq + i;
+    if (row0 + row < nrows) {
+      t.r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)(row0 + row) * row_stride + c * 8);
+    } else {
+      t.r[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Optional RoPE on the staged rows (tokens row0 + row).
+__device__ __forceinline__ void tile_rope(TileRegs& t, const RopeDev& rd, int row0, int nrows, int tid,
+                                          bool inverse) {
+  const int c = tid & 15;
+  const int rq = (tid >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = row0 + rq + i;
+    if (n < nrows) t.r[i] = rope_chunk(rd, token_pos(rd, n), c, t.r[i], inverse);
+  }
+}
+
+__device__ __forceinline__ void tile_store(uint16_t* lds, const TileRegs& t, int tid) {
+  const int c = tid & 15;
+  const int rq = (tid >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rq + i;
+    *reinterpret_cast<u32x4*>(lds + tile_off(row, c * 8)) = t.r[i];
+  }
+}
+
+// 16-byte row fragment: elements [8*chunk, 8*chunk+8) of `row`.
+__device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t* lds, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(lds + tile_off(row, chunk * 8));
+}
+
+// Transposed MFMA operand (32x32x16, A side): lane l gets column col0 + l%32
+// of rows {rbase + 4*(l/32) + e, rbase + 8 + 4*(l/32) + e : e = 0..3}, i.e. the
+// k ordering that matches the register layout of a 32x32 accumulator block
+// whose rows are these tile rows (see mfma_kperm below).  rbase % 16 == 0.
+__device__ __forceinline__ bf16x8 lds_col_frag(const uint16_t* lds, int rbase, int col0, int lane) {
+  const int g = lane >> 4;
+  const int row = rbase + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (lane & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + tile_off(row, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + tile_off(row + 8, col)));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo);
+  const u32x2 b = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32x16 bf16 (fp32 accumulate).  Register layout (lane l, wave64):
+//   A[32 x 16]: lane holds A[l%32][8*(l/32) + t], t = 0..7
+//   B[16 x 32]: lane holds B[8*(l/32) + t][l%32]
+//   C[32 x 32]: lane holds C[8*(j/4) + 4*(l/32) + j%4][l%32], j = 0..15
+// A contraction over the 32 rows of an accumulator block can reuse that
+// block's registers as the k-side operand of the next MFMA if the k index is
+// permuted: accumulator entries j = 8g .. 8g+7 of lane l hold rows
+// 16g + 8*(t/4) + 4*(l/32) + t%4 (t = j - 8g), which is k index 8*(l/32) + t
+// of a 16-deep step when row and k index differ by swapping bits 2 and 3.
+// lds_col_frag reads its 8 rows in exactly that order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pack accumulator entries 8g .. 8g+7 (after an elementwise map already
+// applied) into a bf16x8 k-side operand.
+__device__ __forceinline__ bf16x8 pack_acc8(const float* v) {
+  u32x4 w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) w[t] = pack_bf16(v[2 * t], v[2 * t + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Butterfly across the two 32-lane halves of the wave.
+__device__ __forceinline__ float xor32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+// XCD-aware workgroup order: the hardware deals workgroups round-robin over
+// the 8 XCDs (each with its own L2).  Return a logical index such that every
+// XCD receives a contiguous range of logical indices, so workgroups that share
+// K/V (same batch and head) run on the same XCD.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int NXCD = 8;
+  const int q = total / NXCD;
+  const int r = total % NXCD;
+  const int xcd = wg % NXCD;
+  const int slot = wg / NXCD;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+}  // namespace wanattn

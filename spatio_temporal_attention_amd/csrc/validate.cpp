@@ -1,0 +1,132 @@
+// Host-side argument checks of the wanattn C interface (see validate.h).
+#include "validate.h"
+
+#include <math.h>
+
+namespace wanattn {
+
+int check_dims(int B, int L, int H, int D) {
+  if (B <= 0 || L <= 0 || H <= 0) return WANATTN_ERR_SHAPE;
+  if (D != WANATTN_HEAD_DIM) return WANATTN_ERR_UNSUPPORTED;
+  const int64_t elems = (int64_t)B * L * H * D;
+  if (elems > MAX_TENSOR_ELEMS) return WANATTN_ERR_SHAPE;
+  // workgroups of 128 rows per (b, h) must fit a 1-D grid
+  if ((int64_t)B * H * ((L + 127) / 128) > 0x7fffffff) return WANATTN_ERR_SHAPE;
+  return WANATTN_OK;
+}
+
+int check_rope_only(wanattn_grid g, wanattn_rope r, int D) {
+  if (g.f <= 0 || g.h <= 0 || g.w <= 0) return WANATTN_ERR_SHAPE;
+  if (r.d_f < 0 || r.d_h < 0 || r.d_w < 0) return WANATTN_ERR_UNSUPPORTED;
+  if ((r.d_f | r.d_h | r.d_w) & 1) return WANATTN_ERR_UNSUPPORTED;
+  if ((int64_t)r.d_f + r.d_h + r.d_w != D) return WANATTN_ERR_UNSUPPORTED;
+  if (!(r.theta > 0.f) || !isfinite(r.theta)) return WANATTN_ERR_UNSUPPORTED;
+  return WANATTN_OK;
+}
+
+int check_grid_rope(wanattn_grid g, wanattn_rope r, int L, int D) {
+  const int rc = check_rope_only(g, r, D);
+  if (rc != WANATTN_OK) return rc;
+  if ((int64_t)g.f * g.h * g.w != (int64_t)L) return WANATTN_ERR_SHAPE;
+  return WANATTN_OK;
+}
+
+int check_scale(float scale) { return isfinite(scale) ? WANATTN_OK : WANATTN_ERR_UNSUPPORTED; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t rope_table_entries(wanattn_grid g, wanattn_rope r) {
+  if (check_rope_only(g, r, r.d_f + r.d_h + r.d_w) != WANATTN_OK) return -1;
+  if (r.d_f + r.d_h + r.d_w <= 0) return -1;
+  return (int64_t)g.f * (r.d_f / 2) + (int64_t)g.h * (r.d_h / 2) + (int64_t)g.w * (r.d_w / 2);
+}
+
+size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
+  if (check_dims(B, L, H, D) != WANATTN_OK) return 0;
+  if (!with_rope) return 0;
+  return (size_t)B * L * H * D * 2;   // rotated keys
+}
+
+size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
+  if (check_dims(B, L, H, D) != WANATTN_OK) return 0;
+  size_t delta = (size_t)B * H * L * 4;
+  delta = (delta + 255) & ~(size_t)255;
+  if (!with_rope) return delta;
+  return delta + 2 * (size_t)B * L * H * D * 2;   // + rotated queries and keys
+}
+
+static int check_bf16(const void* p) {
+  if (p == nullptr) return WANATTN_ERR_NULL;
+  return aligned(p, 16) ? WANATTN_OK : WANATTN_ERR_ALIGN;
+}
+
+#define WANATTN_TRY(expr)          \
+  do {                             \
+    const int rc_ = (expr);        \
+    if (rc_ != WANATTN_OK) return rc_; \
+  } while (0)
+
+int validate_rope3d(const void* x, const void* y, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
+                    const float* table) {
+  if (x == nullptr || y == nullptr || table == nullptr) return WANATTN_ERR_NULL;
+  WANATTN_TRY(check_dims(B, L, H, D));
+  WANATTN_TRY(check_grid_rope(g, r, L, D));
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(table, 16)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
+int validate_self_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int L,
+                      int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                      const void* ws, size_t ws_bytes) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return WANATTN_ERR_NULL;
+  WANATTN_TRY(check_dims(B, L, H, D));
+  if (table != nullptr) WANATTN_TRY(check_grid_rope(g, r, L, D));
+  WANATTN_TRY(check_scale(scale));
+  WANATTN_TRY(check_bf16(q));
+  WANATTN_TRY(check_bf16(k));
+  WANATTN_TRY(check_bf16(v));
+  WANATTN_TRY(check_bf16(o));
+  if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
+  if (table != nullptr) {
+    if (!aligned(table, 16)) return WANATTN_ERR_ALIGN;
+    if (ws == nullptr || ws_bytes < self_fwd_ws_bytes(B, L, H, D, 1)) return WANATTN_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
+  }
+  return WANATTN_OK;
+}
+
+int validate_self_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, const void* dq, const void* dk, const void* dv, int B, int L, int H,
+                      int D, wanattn_grid g, wanattn_rope r, const float* table, float scale, const void* ws,
+                      size_t ws_bytes) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return WANATTN_ERR_NULL;
+  WANATTN_TRY(check_dims(B, L, H, D));
+  if (table != nullptr) WANATTN_TRY(check_grid_rope(g, r, L, D));
+  WANATTN_TRY(check_scale(scale));
+  const void* bufs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : bufs) WANATTN_TRY(check_bf16(p));
+  if (!aligned(lse, 4)) return WANATTN_ERR_ALIGN;
+  if (table != nullptr && !aligned(table, 16)) return WANATTN_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < self_bwd_ws_bytes(B, L, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
+int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
+                       const float* lse, int B, int Lq, int Lk, int H, int D, float scale) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return WANATTN_ERR_NULL;
+  WANATTN_TRY(check_dims(B, Lq, H, D));
+  WANATTN_TRY(check_dims(B, Lk, H, D));
+  WANATTN_TRY(check_scale(scale));
+  WANATTN_TRY(check_bf16(q));
+  WANATTN_TRY(check_bf16(k));
+  WANATTN_TRY(check_bf16(v));
+  WANATTN_TRY(check_bf16(o));
+  if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
+  if (k_lens != nullptr && !aligned(k_lens, 4)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
+}  // namespace wanattn

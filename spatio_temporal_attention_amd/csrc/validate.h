@@ -1,0 +1,38 @@
+// Host-side argument checks of the wanattn C interface.  Pure C++ (no HIP),
+// so the rules can be read and tested apart from the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/wanattn.h"
+
+namespace wanattn {
+
+// Largest element count of one [B, L, H, D] tensor the kernels index (64-bit
+// offsets are used throughout; this bounds grids and int32 row counts).
+constexpr int64_t MAX_TENSOR_ELEMS = (int64_t)1 << 40;
+
+int check_dims(int B, int L, int H, int D);
+int check_grid_rope(wanattn_grid g, wanattn_rope r, int L, int D);
+int check_rope_only(wanattn_grid g, wanattn_rope r, int D);
+int check_scale(float scale);
+bool aligned(const void* p, size_t a);
+int64_t rope_table_entries(wanattn_grid g, wanattn_rope r);   // (cos, sin) pairs; -1 if invalid
+
+size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);
+size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope);
+
+int validate_rope3d(const void* x, const void* y, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
+                    const float* table);
+int validate_self_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int L,
+                      int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                      const void* ws, size_t ws_bytes);
+int validate_self_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, const void* dq, const void* dk, const void* dv, int B, int L, int H,
+                      int D, wanattn_grid g, wanattn_rope r, const float* table, float scale, const void* ws,
+                      size_t ws_bytes);
+int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
+                       const float* lse, int B, int Lq, int Lk, int H, int D, float scale);
+
+}  // namespace wanattn

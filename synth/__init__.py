@@ -136,3 +136,16 @@ def random_bf16(seed: int, shape, scale: float = 1.0) -> np.ndarray:
 def sample_rows(seed: int, n: int, r: int) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     return np.sort(rng.choice(n, size=min(r, n), replace=False))
+
+
+def make_text_context(index: int, B: int, H: int, Lk: int = 512, D: int = 128, k_len_range=(20, 512)):
+    """Text-token keys/values [B, Lk, H, D] (bf16 bits) and valid lengths [B] drawn like workload 3,
+    from workload `index`'s seed (streams spawned after the standard ones)."""
+    children = np.random.SeedSequence(SEED_BASE + index).spawn(len(STREAMS) + 3)[len(STREAMS):]
+    gk, gv, gl = (np.random.Generator(np.random.PCG64(s)) for s in children)
+    lo, hi = k_len_range
+    return {
+        "k": normal_bf16(gk, (B, Lk, H, D)),
+        "v": normal_bf16(gv, (B, Lk, H, D)),
+        "k_lens": gl.integers(lo, hi + 1, size=B, dtype=np.int64).astype(np.int32),
+    }

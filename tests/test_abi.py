@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host with the documented
+status codes (validation runs before anything is enqueued, so these calls
+never reach the GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import spatio_temporal_attention_amd as wa
+from spatio_temporal_attention_amd import Grid, Rope
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wanattn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+P = 0x10000          # a 16-byte-aligned stand-in address; never dereferenced by validation
+ODD = 0x10008        # 8-byte aligned only
+GRID = Grid(5, 8, 8)
+ROPE = Rope(48, 40, 40, 10000.0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(wa.LIB_PATH):
+        from spatio_temporal_attention_amd import build
+        build.build()
+    return wa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wanattn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libwanattn.so"
+        assert n in wa._SIGNATURES, f"{n} has no binding"
+
+
+def test_strerror(lib):
+    for code in range(7):
+        s = lib.wanattn_strerror(code).decode()
+        assert s.startswith("wanattn:")
+    assert "unknown" in lib.wanattn_strerror(99).decode()
+
+
+def test_rope_table_bytes(lib):
+    assert lib.wanattn_rope_table_bytes(Grid(21, 45, 80), ROPE) == 8 * (21 * 24 + 45 * 20 + 80 * 20)
+    assert lib.wanattn_rope_table_bytes(Grid(64, 64, 64), ROPE) == 8 * 64 * 64
+    assert lib.wanattn_rope_table_bytes(Grid(0, 45, 80), ROPE) == 0
+    assert lib.wanattn_rope_table_bytes(GRID, Rope(47, 41, 40, 1e4)) == 0
+    assert lib.wanattn_rope_table_bytes(GRID, Rope(48, 40, 40, -1.0)) == 0
+
+
+def test_workspace_sizes(lib):
+    B, L, H, D = 1, 75600, 40, 128
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == B * L * H * D * 2
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 0
+    delta = (B * H * L * 4 + 255) // 256 * 256
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 2 * B * L * H * D * 2
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, 64, 1) == 0
+
+
+def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P, scale=0.088,
+         ws=P, ws_bytes=1 << 30):
+    return lib.wanattn_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes, None)
+
+
+def test_self_fwd_validation(lib):
+    assert _fwd(lib, q=None) == NULL
+    assert _fwd(lib, o=None) == NULL
+    assert _fwd(lib, L=0) == SHAPE
+    assert _fwd(lib, B=-1) == SHAPE
+    assert _fwd(lib, D=64) == UNSUP
+    assert _fwd(lib, L=321) == SHAPE                          # f*h*w != L
+    assert _fwd(lib, r=Rope(48, 40, 38, 1e4)) == UNSUP         # split does not sum to D
+    assert _fwd(lib, r=Rope(47, 41, 40, 1e4)) == UNSUP         # odd width
+    assert _fwd(lib, r=Rope(48, 40, 40, 0.0)) == UNSUP         # theta <= 0
+    assert _fwd(lib, scale=float("nan")) == UNSUP
+    assert _fwd(lib, scale=float("inf")) == UNSUP
+    assert _fwd(lib, q=ODD) == ALIGN
+    assert _fwd(lib, lse=P + 2) == ALIGN
+    assert _fwd(lib, table=ODD) == ALIGN
+    assert _fwd(lib, ws=None) == WS
+    assert _fwd(lib, ws_bytes=320 * 2 * 128 * 2 - 1) == WS
+    assert _fwd(lib, L=1 << 30, g=Grid(1 << 10, 1 << 10, 1 << 10), H=1 << 14) == SHAPE   # too large
+
+
+def test_self_bwd_validation(lib):
+    def bwd(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE,
+                 table=P, scale=0.088, ws=P, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.wanattn_self_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                    a["B"], a["L"], a["H"], a["D"], a["g"], a["r"], a["table"], a["scale"],
+                                    a["ws"], a["ws_bytes"], None)
+    assert bwd(lse=None) == NULL
+    assert bwd(dv=None) == NULL
+    assert bwd(D=256) == UNSUP
+    assert bwd(g=Grid(5, 8, 7)) == SHAPE
+    assert bwd(dk=ODD) == ALIGN
+    assert bwd(ws=None) == WS
+    need = lib.wanattn_self_bwd_workspace_bytes(1, 320, 2, 128, 1)
+    assert bwd(ws_bytes=need - 1) == WS
+    assert bwd(table=None, ws_bytes=lib.wanattn_self_bwd_workspace_bytes(1, 320, 2, 128, 0) - 1) == WS
+
+
+def test_cross_and_rope_validation(lib):
+    def cross(**kw):
+        a = dict(q=P, k=P, v=P, kl=P, o=P, lse=P, B=2, Lq=100, Lk=512, H=2, D=128, scale=0.088)
+        a.update(kw)
+        return lib.wanattn_cross_fwd(a["q"], a["k"], a["v"], a["kl"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                                     a["H"], a["D"], a["scale"], None)
+    assert cross(v=None) == NULL
+    assert cross(Lk=0) == SHAPE
+    assert cross(Lq=-5) == SHAPE
+    assert cross(D=127) == UNSUP
+    assert cross(kl=P + 1) == ALIGN
+    assert cross(scale=float("nan")) == UNSUP
+
+    def rope(**kw):
+        a = dict(x=P, y=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P, inv=0)
+        a.update(kw)
+        return lib.wanattn_rope3d(a["x"], a["y"], a["B"], a["L"], a["H"], a["D"], a["g"], a["r"], a["table"],
+                                  a["inv"], None)
+    assert rope(table=None) == NULL
+    assert rope(L=300) == SHAPE
+    assert rope(y=ODD) == ALIGN
+    assert rope(r=Rope(48, 40, 40, float("inf"))) == UNSUP
+    assert lib.wanattn_rope_table_init(None, GRID, ROPE, None) == NULL
+    assert lib.wanattn_rope_table_init(P, Grid(0, 1, 1), ROPE, None) == SHAPE
+    assert lib.wanattn_rope_table_init(ODD, GRID, ROPE, None) == ALIGN
+
+
+def test_binding_token_grid_matches_golden():
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "token_grids.json")))["cases"]
+    for c in cases:
+        assert list(wa.token_grid(c["frames"], c["height"], c["width"])) == c["grid"]
+    with pytest.raises(ValueError):
+        wa.token_grid(80, 480, 832)

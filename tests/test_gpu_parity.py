@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C-ABI binding) against the fp64 oracle.
+
+Inputs are the seeded synthetic workloads of `synth` (the same host arrays feed
+both sides).  Bar (bf16 I/O, fp32 statistics): max-abs <= 2e-2 and relative
+L2 <= 5e-3 on O, dQ, dK, dV; |LSE error| <= 1e-3.  Large workloads are checked
+on 64 seeded rows per (batch, head).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bf16_to_f64, check_close, check_lse, f32_to_np, to_dev
+from oracle import RopeSpec
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import spatio_temporal_attention_amd as wa  # noqa: E402
+
+ROPE = RopeSpec()
+SCALE = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    wa.lib()   # the compiled library must be present: no fallback exists
+
+
+def _f64(bits):
+    return synth.bf16_bits_to_f64(bits)
+
+
+def _table(grid):
+    return wa.rope_table(grid, ROPE)
+
+
+# ---------------------------------------------------------------------------
+# RoPE table and standalone rotation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", [(5, 8, 8), (21, 30, 52), (21, 45, 80), (64, 64, 64), (1, 1, 1)])
+def test_rope_table_matches_oracle(grid):
+    got = _table(grid).cpu().numpy().astype(np.float64)
+    ref = np.concatenate([t.reshape(-1) for t in oracle.rope_table_ref(grid, ROPE)])
+    assert got.shape == ref.shape
+    err = np.abs(got - ref).max()
+    print(f"  table {grid}: max_abs={err:.3e}")
+    assert err <= 6e-8     # fp32 rounding of |cos|, |sin| <= 1
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+def test_rope3d_matches_oracle(inverse):
+    grid = (5, 8, 8)
+    bits = synth.random_bf16(101, (2, 320, 3, 128), scale=2.0)
+    x = to_dev(bits)
+    y = wa.rope3d(x, grid, _table(grid), ROPE, inverse=inverse)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(y)
+    ref = oracle.rope3d_ref(_f64(bits), grid, ROPE, inverse=inverse)
+    # one bf16 rounding (half an ulp, 2^-9 relative) of an fp32 result: the bar is relative per
+    # element (inputs have sigma 2, so an absolute bar would only measure the bf16 ulp of large values)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+    check_close("rope3d", got, ref, max_abs=np.inf)
+    # in place gives the same bits
+    wa.rope3d(x, grid, _table(grid), ROPE, inverse=inverse, out=x)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_rope3d_round_trip():
+    grid = (3, 4, 5)
+    bits = synth.random_bf16(102, (1, 60, 4, 128))
+    x = to_dev(bits)
+    t = _table(grid)
+    back = wa.rope3d(wa.rope3d(x, grid, t, ROPE), grid, t, ROPE, inverse=True)
+    torch.cuda.synchronize()
+    x64 = _f64(bits)
+    # two roundings of at most 2^-9 of the rotated pair's norm each; rotation preserves that norm
+    # and spreads the error over both elements of the pair
+    pair = np.sqrt(x64[..., 0::2] ** 2 + x64[..., 1::2] ** 2).repeat(2, axis=-1)
+    assert np.all(np.abs(bf16_to_f64(back) - x64) <= 2.0 ** -7 * pair + 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Self-attention forward
+# ---------------------------------------------------------------------------
+
+def _run_self_fwd(qb, kb, vb, grid, rope_on, scale=SCALE):
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    table = _table(grid) if rope_on else None
+    o, lse = wa.self_fwd(q, k, v, grid=grid, table=table, rope=ROPE, scale=scale)
+    torch.cuda.synchronize()
+    return bf16_to_f64(o), f32_to_np(lse)
+
+
+def test_self_fwd_tiny_workload():
+    w = synth.WORKLOADS[1]
+    inp = synth.make_inputs(1)
+    o, lse = _run_self_fwd(inp["q"], inp["k"], inp["v"], w.grid, True)
+    ro, rl = oracle.self_fwd_ref(_f64(inp["q"]), _f64(inp["k"]), _f64(inp["v"]), SCALE, w.grid, ROPE)
+    check_close("O", o, ro)
+    check_lse("LSE", lse, rl)
+
+
+@pytest.mark.parametrize("B,grid,H,rope_on,qmul", [
+    (2, (2, 10, 10), 3, True, 1.0),     # L = 200: ragged against 64-key tiles and 128-row tiles
+    (1, (1, 1, 1), 2, True, 1.0),       # a single token
+    (1, (3, 5, 7), 2, False, 1.0),      # L = 105, no rotary
+    (1, (4, 8, 8), 2, True, 8.0),       # peaked softmax: exercises the running-max rescale
+    (3, (1, 9, 15), 1, True, 3.0),      # B > 1, L = 135
+])
+def test_self_fwd_small(B, grid, H, rope_on, qmul):
+    L = int(np.prod(grid))
+    seed = 1000 + L + B
+    qb = synth.random_bf16(seed, (B, L, H, 128), scale=qmul)
+    kb = synth.random_bf16(seed + 1, (B, L, H, 128))
+    vb = synth.random_bf16(seed + 2, (B, L, H, 128))
+    o, lse = _run_self_fwd(qb, kb, vb, grid, rope_on)
+    ro, rl = oracle.self_fwd_ref(_f64(qb), _f64(kb), _f64(vb), SCALE, grid, ROPE if rope_on else None)
+    check_close("O", o, ro)
+    check_lse("LSE", lse, rl)
+
+
+def test_self_fwd_scale_zero_closed_form():
+    grid = (5, 8, 8)
+    qb, kb, vb = (synth.random_bf16(s, (1, 320, 2, 128)) for s in (201, 202, 203))
+    o, lse = _run_self_fwd(qb, kb, vb, grid, True, scale=0.0)
+    mean_v = _f64(vb).mean(axis=1, keepdims=True)
+    check_close("O", o, np.broadcast_to(mean_v, o.shape))
+    check_lse("LSE", lse, np.full(lse.shape, math.log(320)))
+
+
+def _sampled_self_fwd_check(index):
+    w = synth.WORKLOADS[index]
+    inp = synth.make_inputs(index, with_dout=False)
+    print(f"  workload {index} ({w.name}): generated", flush=True)
+    o, lse = _run_self_fwd(inp["q"], inp["k"], inp["v"], w.grid, True)
+    print(f"  workload {index}: GPU done", flush=True)
+    rows = inp["rows"]
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+            ro, rl = oracle.self_fwd_ref(_f64(inp["q"][sl]), _f64(inp["k"][sl]), _f64(inp["v"][sl]), SCALE,
+                                         w.grid, ROPE, rows=rows[b:b + 1, h:h + 1])
+            got_o.append(o[b, rows[b, h], h])
+            ref_o.append(ro[0, 0])
+            got_l.append(lse[b, h, rows[b, h]])
+            ref_l.append(rl[0, 0])
+    check_close("O (sampled)", np.stack(got_o), np.stack(ref_o))
+    check_lse("LSE (sampled)", np.stack(got_l), np.stack(ref_l))
+
+
+def test_self_fwd_480p_sampled():
+    _sampled_self_fwd_check(2)
+
+
+def test_self_fwd_720p_sampled():
+    _sampled_self_fwd_check(4)
+
+
+# ---------------------------------------------------------------------------
+# Cross-attention forward
+# ---------------------------------------------------------------------------
+
+def _run_cross(qb, kb, vb, lens, scale=SCALE):
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    kl = None if lens is None else torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    o, lse = wa.cross_fwd(q, k, v, kl, scale=scale)
+    torch.cuda.synchronize()
+    return bf16_to_f64(o), f32_to_np(lse)
+
+
+def test_cross_workload_sampled():
+    w = synth.WORKLOADS[3]
+    inp = synth.make_inputs(3)
+    o, lse = _run_cross(inp["q"], inp["k"], inp["v"], inp["k_lens"])
+    rows = inp["rows"]
+    ro, rl = oracle.cross_fwd_ref(_f64(inp["q"]), _f64(inp["k"]), _f64(inp["v"]), inp["k_lens"], SCALE, rows=rows)
+    got_o = np.stack([[o[b, rows[b, h], h] for h in range(w.H)] for b in range(w.B)])
+    got_l = np.stack([[lse[b, h, rows[b, h]] for h in range(w.H)] for b in range(w.B)])
+    check_close("O (sampled)", got_o, ro)
+    check_lse("LSE (sampled)", got_l, rl)
+
+
+def test_cross_masking_edge_cases():
+    B, Lq, Lk, H = 4, 150, 100, 2
+    qb = synth.random_bf16(301, (B, Lq, H, 128))
+    kb = synth.random_bf16(302, (B, Lk, H, 128))
+    vb = synth.random_bf16(303, (B, Lk, H, 128))
+    lens = np.array([1, 100, 37, 64], dtype=np.int32)
+    # padded keys hold NaN: they must never reach an output
+    kb_nan, vb_nan = kb.copy(), vb.copy()
+    for b, n in enumerate(lens):
+        kb_nan[b, n:] = 0x7FC0
+        vb_nan[b, n:] = 0x7FC0
+    o, lse = _run_cross(qb, kb_nan, vb_nan, lens)
+    ro, rl = oracle.cross_fwd_ref(_f64(qb), _f64(kb), _f64(vb), lens, SCALE)
+    check_close("O", o, ro)
+    check_lse("LSE", lse, rl)
+    # k_len = 1: O is exactly v_0 up to bf16 output rounding
+    np.testing.assert_allclose(o[0], np.broadcast_to(_f64(vb)[0, :1], o[0].shape), atol=2e-2)
+
+
+def test_cross_all_valid_and_empty():
+    B, Lq, Lk, H = 2, 70, 512, 3
+    qb = synth.random_bf16(311, (B, Lq, H, 128))
+    kb = synth.random_bf16(312, (B, Lk, H, 128))
+    vb = synth.random_bf16(313, (B, Lk, H, 128))
+    o, lse = _run_cross(qb, kb, vb, None)
+    ro, rl = oracle.cross_fwd_ref(_f64(qb), _f64(kb), _f64(vb), None, SCALE)
+    check_close("O (no mask)", o, ro)
+    check_lse("LSE (no mask)", lse, rl)
+    o2, lse2 = _run_cross(qb, kb, vb, [Lk, 0])
+    check_close("O (k_len = Lk)", o2[0], ro[0])
+    assert np.all(o2[1] == 0.0) and np.all(np.isneginf(lse2[1]))
+
+
+def test_cross_scale_zero():
+    B, Lq, Lk, H = 2, 33, 40, 1
+    qb, kb, vb = (synth.random_bf16(s, (B, L, H, 128)) for s, L in ((321, Lq), (322, Lk), (323, Lk)))
+    lens = [7, 40]
+    o, lse = _run_cross(qb, kb, vb, lens, scale=0.0)
+    for b, n in enumerate(lens):
+        check_close("O", o[b], np.broadcast_to(_f64(vb)[b, :n].mean(axis=0), o[b].shape))
+        check_lse("LSE", lse[b], np.full(lse[b].shape, math.log(n)))
+
+
+# ---------------------------------------------------------------------------
+# Self-attention backward
+# ---------------------------------------------------------------------------
+
+def _run_self_bwd(qb, kb, vb, dob, grid, rope_on, scale=SCALE):
+    q, k, v, do = to_dev(qb), to_dev(kb), to_dev(vb), to_dev(dob)
+    table = _table(grid) if rope_on else None
+    o, lse = wa.self_fwd(q, k, v, grid=grid, table=table, rope=ROPE, scale=scale)
+    dq, dk, dv = wa.self_bwd(q, k, v, o, lse, do, grid=grid, table=table, rope=ROPE, scale=scale)
+    torch.cuda.synchronize()
+    return bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+
+
+def test_self_bwd_tiny_workload():
+    w = synth.WORKLOADS[1]
+    inp = synth.make_inputs(1)
+    dq, dk, dv = _run_self_bwd(inp["q"], inp["k"], inp["v"], inp["dout"], w.grid, True)
+    rq, rk, rv = oracle.self_bwd_ref(_f64(inp["q"]), _f64(inp["k"]), _f64(inp["v"]), _f64(inp["dout"]), SCALE,
+                                     w.grid, ROPE)
+    check_close("dQ", dq, rq)
+    check_close("dK", dk, rk)
+    check_close("dV", dv, rv)
+
+
+@pytest.mark.parametrize("B,grid,H,rope_on,qmul", [
+    (2, (2, 10, 10), 2, True, 1.0),
+    (1, (3, 5, 7), 1, False, 1.0),
+    (1, (4, 8, 8), 2, True, 4.0),
+    (1, (1, 1, 1), 1, True, 1.0),
+])
+def test_self_bwd_small(B, grid, H, rope_on, qmul):
+    L = int(np.prod(grid))
+    seed = 2000 + L + B
+    qb = synth.random_bf16(seed, (B, L, H, 128), scale=qmul)
+    kb, vb, dob = (synth.random_bf16(seed + i, (B, L, H, 128)) for i in (1, 2, 3))
+    dq, dk, dv = _run_self_bwd(qb, kb, vb, dob, grid, rope_on)
+    rq, rk, rv = oracle.self_bwd_ref(_f64(qb), _f64(kb), _f64(vb), _f64(dob), SCALE, grid,
+                                     ROPE if rope_on else None)
+    check_close("dQ", dq, rq)
+    check_close("dK", dk, rk)
+    check_close("dV", dv, rv)
+
+
+def test_self_bwd_720p_sampled():
+    w = synth.WORKLOADS[4]
+    inp = synth.make_inputs(4)
+    print("  720p: generated", flush=True)
+    dq, dk, dv = _run_self_bwd(inp["q"], inp["k"], inp["v"], inp["dout"], w.grid, True)
+    print("  720p: GPU done", flush=True)
+    rows = inp["rows"]
+    got, ref = [], []
+    for h in range(w.H):
+        sl = (slice(0, 1), slice(None), slice(h, h + 1))
+        r = oracle.self_bwd_dq_rows(_f64(inp["q"][sl]), _f64(inp["k"][sl]), _f64(inp["v"][sl]),
+                                    _f64(inp["dout"][sl]), SCALE, w.grid, ROPE, rows[:, h:h + 1])
+        got.append(dq[0, rows[0, h], h])
+        ref.append(r[0, 0])
+    check_close("dQ (sampled, all heads)", np.stack(got), np.stack(ref))
+    # dK/dV on sampled key rows need every query row's statistics: one head here.
+    h = int(synth.sample_rows(404, w.H, 1)[0])
+    sl = (slice(0, 1), slice(None), slice(h, h + 1))
+    rk, rv = oracle.self_bwd_dkdv_rows(_f64(inp["q"][sl]), _f64(inp["k"][sl]), _f64(inp["v"][sl]),
+                                       _f64(inp["dout"][sl]), SCALE, w.grid, ROPE, rows[:, h:h + 1], block=1024)
+    check_close(f"dK (sampled, head {h})", dk[0, rows[0, h], h], rk[0, 0])
+    check_close(f"dV (sampled, head {h})", dv[0, rows[0, h], h], rv[0, 0])
