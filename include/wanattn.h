@@ -32,8 +32,10 @@
  *      y[2j]   = x[2j] cos - x[2j+1] sin,   y[2j+1] = x[2j] sin + x[2j+1] cos.
  *    Each width must be even and >= 0, d_f + d_h + d_w == D, theta > 0.
  *  Rounding.  All arithmetic is fp32 (MFMA accumulates bf16 products in fp32);
- *    every fp32 -> bf16 rounding is round-to-nearest-even.  Rotated q/k are
- *    rounded to bf16 before the score products.
+ *    every fp32 -> bf16 rounding is round-to-nearest-even.  Rotated keys are
+ *    rounded to bf16 before the score products; a rotated query is carried as
+ *    a bf16 pair hi + lo (hi = RNE(x), lo = RNE(x - hi)), so scores lose
+ *    precision only to the keys' rounding.
  *  Memory.  Every pointer is device memory owned by the caller, which keeps it
  *    alive until the stream's work has finished.  bf16 buffers, the rope table
  *    and workspaces must be 16-byte aligned; fp32 and int32 buffers 4-byte
@@ -136,7 +138,8 @@ int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float
  *   dq_i = R(p_i)^T scale sum_j dS_ij R(p_j) k_j;  dk_j = R(p_j)^T scale sum_i dS_ij R(p_i) q_i.
  * Gradients are with respect to the unrotated q and k.  table == NULL: no RoPE.
  * Workspace: wanattn_self_bwd_workspace_bytes bytes (Delta fp32 [B, H, L], and
- * with a table the rotated q and k, bf16 [B, L, H, D] each).
+ * with a table the rotated q as a bf16 hi/lo pair and the rotated k, three
+ * bf16 [B, L, H, D] tensors).
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 

@@ -127,14 +127,19 @@ WANATTN_API int wanattn_self_bwd(const void* q, const void* k, const void* v, co
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.rope = make_rope(g, r, table);
+  p.q_lo = nullptr;
   if (table != nullptr) {
-    uint16_t* qr = (uint16_t*)((char*)ws + delta_bytes);
-    uint16_t* kr = qr + (size_t)B * L * H * D;
-    int e = hip_status(launch_rope3d((const uint16_t*)q, qr, B, L, H, p.rope, false, s));
+    // Rotated queries as bf16 hi + lo (exactly as the forward rotated them),
+    // rotated keys as bf16: the recomputed scores match the forward's.
+    uint16_t* qh = (uint16_t*)((char*)ws + delta_bytes);
+    uint16_t* ql = qh + (size_t)B * L * H * D;
+    uint16_t* kr = ql + (size_t)B * L * H * D;
+    int e = hip_status(launch_rope3d_split((const uint16_t*)q, qh, ql, B, L, H, p.rope, s));
     if (e != WANATTN_OK) return e;
     e = hip_status(launch_rope3d((const uint16_t*)k, kr, B, L, H, p.rope, false, s));
     if (e != WANATTN_OK) return e;
-    p.q = qr;
+    p.q = qh;
+    p.q_lo = ql;
     p.k = kr;
   }
   p.v = (const uint16_t*)v;

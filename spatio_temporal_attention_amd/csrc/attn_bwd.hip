@@ -9,8 +9,10 @@
 //   dS_ij   = P_ij (<dO_i, v_j> - Delta_i)
 //   dq~_i   = scale sum_j dS_ij k~_j,   dk~_j = scale sum_i dS_ij q~_i
 //   dq_i    = R(p_i)^T dq~_i,           dk_j  = R(p_j)^T dk~_j
-// q~ and k~ arrive pre-rotated; the inverse rotation is fused into the dQ and
-// dK stores.
+// q~ and k~ arrive pre-rotated (q~ as a bf16 hi + lo pair, exactly as the
+// forward used it, so the recomputed P matches the forward's LSE); the inverse
+// rotation is fused into the dQ and dK stores.  Tiles move global -> LDS by
+// direct loads (global_load_lds), double-buffered.
 //
 //  * bwd_delta: Delta per row (memory-bound).
 //  * bwd_dkdv:  workgroup = 128 keys (4 waves x 32), loop over 64-query tiles.
@@ -74,9 +76,12 @@ __device__ __forceinline__ void store_grad4(uint16_t* row_ptr, const RopeDev& ro
 
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup owns 128 keys; loop over query tiles of 64.
+// SPLIT: rotated queries come as bf16 hi + lo; S takes both (as the forward did).
 // ---------------------------------------------------------------------------
+template <bool SPLIT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE_ELEMS];   // [buffer][Q~ | dO]
+  constexpr int NT = SPLIT ? 3 : 2;                                           // Q~ hi, [Q~ lo], dO
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][NT][TILE_ELEMS];
   __shared__ float lse2_s[2][TILE_ROWS];                                      // LSE * log2 e (+inf: no row)
   __shared__ float delta_s[2][TILE_ROWS];
 
@@ -85,6 +90,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % p.n_tiles;
@@ -95,6 +101,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int64_t rs = (int64_t)p.H * HD;
   const int64_t head_off = ((int64_t)b * p.L * p.H + h) * HD;
   const uint16_t* qbase = p.q + head_off;
+  const uint16_t* qlbase = SPLIT ? p.q_lo + head_off : nullptr;
   const uint16_t* dobase = p.dout + head_off;
   const float* lse_row = p.lse + ((int64_t)b * p.H + h) * p.L;
   const float* delta_row = p.delta + ((int64_t)b * p.H + h) * p.L;
@@ -123,7 +130,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const float c2 = p.scale_log2;
   const int n_qt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
 
-  auto load_stats = [&](int buf, int row0) {
+  auto stage = [&](int buf, int row0) {
+    tile_dma(tiles[buf][0], qbase, rs, row0, p.L, wv, lane);
+    if (SPLIT) tile_dma(tiles[buf][1], qlbase, rs, row0, p.L, wv, lane);
+    tile_dma(tiles[buf][NT - 1], dobase, rs, row0, p.L, wv, lane);
     if (tid < TILE_ROWS) {
       const int i = row0 + tid;
       lse2_s[buf][tid] = (i < p.L) ? lse_row[i] * LOG2E : INFINITY;
@@ -133,23 +143,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  TileRegs qr, dr;
-  tile_load(qr, qbase, rs, 0, p.L, tid);
-  tile_load(dr, dobase, rs, 0, p.L, tid);
-  tile_store(tiles[0][0], qr, tid);
-  tile_store(tiles[0][1], dr, tid);
-  load_stats(0, 0);
+  stage(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int t = 0; t < n_qt; ++t) {
     const int buf = t & 1;
     const bool has_next = t + 1 < n_qt;
-    if (has_next) {
-      tile_load(qr, qbase, rs, (t + 1) * TILE_ROWS, p.L, tid);
-      tile_load(dr, dobase, rs, (t + 1) * TILE_ROWS, p.L, tid);
-    }
+    if (has_next) stage(buf ^ 1, (t + 1) * TILE_ROWS);
     const uint16_t* qs = tiles[buf][0];
-    const uint16_t* ds_ = tiles[buf][1];
+    const uint16_t* qls = tiles[buf][SPLIT ? 1 : 0];
+    const uint16_t* ds_ = tiles[buf][NT - 1];
 
     bf16x8 pf[4], dsf[4];
 #pragma unroll
@@ -158,6 +162,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         s_acc = mfma32(lds_row_frag(qs, qb * 32 + col, 2 * s + half), kf[s], s_acc);
+        if (SPLIT) s_acc = mfma32(lds_row_frag(qls, qb * 32 + col, 2 * s + half), kf[s], s_acc);
         dp_acc = mfma32(lds_row_frag(ds_, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
       }
       float pv[16], dsv[16];
@@ -182,11 +187,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
 
-    if (has_next) {
-      tile_store(tiles[buf ^ 1][0], qr, tid);
-      tile_store(tiles[buf ^ 1][1], dr, tid);
-      load_stats(buf ^ 1, (t + 1) * TILE_ROWS);
-    }
+    if (has_next) wait_vmem();
     __syncthreads();
   }
 
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup owns 128 queries; loop over key tiles of 64.
 // ---------------------------------------------------------------------------
+template <bool SPLIT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE_ELEMS];   // [buffer][K~ | V]
 
@@ -222,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = logical % p.n_tiles;
@@ -237,15 +240,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int i = qt * 128 + wave * 32 + col;
   const bool row_ok = i < p.L;
   bf16x8 qf[8], dof[8];
+  bf16x8 ql[SPLIT ? 8 : 1];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    u32x4 xq = u32x4{0u, 0u, 0u, 0u}, xd = u32x4{0u, 0u, 0u, 0u};
+    u32x4 xq = u32x4{0u, 0u, 0u, 0u}, xd = u32x4{0u, 0u, 0u, 0u}, xl = u32x4{0u, 0u, 0u, 0u};
     if (row_ok) {
-      xq = *reinterpret_cast<const u32x4*>(p.q + head_off + (int64_t)i * rs + (2 * s + half) * 8);
-      xd = *reinterpret_cast<const u32x4*>(p.dout + head_off + (int64_t)i * rs + (2 * s + half) * 8);
+      const int64_t off = head_off + (int64_t)i * rs + (2 * s + half) * 8;
+      xq = *reinterpret_cast<const u32x4*>(p.q + off);
+      xd = *reinterpret_cast<const u32x4*>(p.dout + off);
+      if (SPLIT) xl = *reinterpret_cast<const u32x4*>(p.q_lo + off);
     }
     qf[s] = __builtin_bit_cast(bf16x8, xq);
     dof[s] = __builtin_bit_cast(bf16x8, xd);
+    if (SPLIT) ql[s] = __builtin_bit_cast(bf16x8, xl);
   }
   const int64_t stat = ((int64_t)b * p.H + h) * p.L + i;
   const float lse2 = row_ok ? p.lse[stat] * LOG2E : INFINITY;
@@ -257,19 +264,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   for (int d = 0; d < 4; ++d) dq_acc[d] = f32x16{};
   const int n_kt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
 
-  TileRegs kr, vr;
-  tile_load(kr, kbase, rs, 0, p.L, tid);
-  tile_load(vr, vbase, rs, 0, p.L, tid);
-  tile_store(tiles[0][0], kr, tid);
-  tile_store(tiles[0][1], vr, tid);
+  tile_dma(tiles[0][0], kbase, rs, 0, p.L, wv, lane);
+  tile_dma(tiles[0][1], vbase, rs, 0, p.L, wv, lane);
+  wait_vmem();
   __syncthreads();
 
   for (int t = 0; t < n_kt; ++t) {
     const int buf = t & 1;
     const bool has_next = t + 1 < n_kt;
     if (has_next) {
-      tile_load(kr, kbase, rs, (t + 1) * TILE_ROWS, p.L, tid);
-      tile_load(vr, vbase, rs, (t + 1) * TILE_ROWS, p.L, tid);
+      tile_dma(tiles[buf ^ 1][0], kbase, rs, (t + 1) * TILE_ROWS, p.L, wv, lane);
+      tile_dma(tiles[buf ^ 1][1], vbase, rs, (t + 1) * TILE_ROWS, p.L, wv, lane);
     }
     const uint16_t* ks = tiles[buf][0];
     const uint16_t* vs = tiles[buf][1];
@@ -282,7 +287,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        s_acc = mfma32(lds_row_frag(ks, kb * 32 + col, 2 * s + half), qf[s], s_acc);
+        const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
+        s_acc = mfma32(a, qf[s], s_acc);
+        if (SPLIT) s_acc = mfma32(a, ql[s], s_acc);
         dp_acc = mfma32(lds_row_frag(vs, kb * 32 + col, 2 * s + half), dof[s], dp_acc);
       }
       float dsv[16];
@@ -306,10 +313,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       }
     }
 
-    if (has_next) {
-      tile_store(tiles[buf ^ 1][0], kr, tid);
-      tile_store(tiles[buf ^ 1][1], vr, tid);
-    }
+    if (has_next) wait_vmem();
     __syncthreads();
   }
 
@@ -344,7 +348,8 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
   q.n_tiles = (p.L + 127) / 128;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)total), dim3(256), 0, stream, q);
+  if (p.q_lo != nullptr) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, q);
+  else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -353,7 +358,8 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
   q.n_tiles = (p.L + 127) / 128;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)total), dim3(256), 0, stream, q);
+  if (p.q_lo != nullptr) hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, q);
+  else hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -12,9 +12,13 @@
 //  * each wave keeps its 32 rotated query rows in registers as the B operand
 //    of S^T = K Q^T (bf16 MFMA 32x32x16), so every lane owns one query row and
 //    the softmax needs one cross-lane step (lane l <-> l^32) per tile;
-//  * K and V tiles of 64 keys are staged through LDS (row-major, swizzled),
-//    double-buffered: the next tile's global loads are in flight while the
-//    current one is multiplied;
+//  * SPLIT_Q (with RoPE): the rotated query is held as bf16 hi + lo and S^T
+//    takes two MFMAs per step.  A single bf16 rounding of the rotated query
+//    moves LSE by up to ~1.2e-3 at 720p (tail of the row distribution); with
+//    the pair the error is set by the keys' rounding alone (~5e-5);
+//  * K and V tiles of 64 keys go global -> LDS directly (global_load_lds,
+//    row-major, swizzled), double-buffered: the next tile's loads are in
+//    flight while the current one is multiplied;
 //  * O^T += V^T P^T reads V through the LDS transpose read and takes P
 //    straight from the S^T accumulator registers (bf16, RNE);
 //  * online softmax in fp32 in the log2 domain (scale * log2 e folded in);
@@ -31,7 +35,7 @@ constexpr int FWD_WAVES = 4;
 constexpr int FWD_BR = 32 * FWD_WAVES;   // query rows per workgroup
 constexpr int FWD_BC = TILE_ROWS;         // keys per tile
 
-template <bool POS_SCALE>
+template <bool POS_SCALE, bool SPLIT_Q>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE_ELEMS];   // [buffer][K|V]
 
@@ -59,18 +63,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   const int i = qt * FWD_BR + wave * 32 + col;
   const bool row_ok = i < p.Lq;
   bf16x8 qf[8];
+  bf16x8 ql[SPLIT_Q ? 8 : 1];
   {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      u32x4 xl = u32x4{0u, 0u, 0u, 0u};
       const int c = 2 * s + half;
       if (row_ok) {
         x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
-        if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
+        if (SPLIT_Q) rope_chunk_split(p.rope, pos, c, x, x, xl);
+        else if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
       }
       qf[s] = __builtin_bit_cast(bf16x8, x);
+      if (SPLIT_Q) ql[s] = __builtin_bit_cast(bf16x8, xl);
     }
   }
 
@@ -83,99 +91,97 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 
-  if (n_tiles > 0) {
-    TileRegs kr, vr;
-    tile_load(kr, kbase, q_row_stride, 0, n_keys, tid);
-    tile_load(vr, vbase, q_row_stride, 0, n_keys, tid);
-    tile_store(smem[0][0], kr, tid);
-    tile_store(smem[0][1], vr, tid);
-    __syncthreads();
+  // One 64-key tile: scores, online softmax, O += P V.
+  auto tile_step = [&](const uint16_t* ks, const uint16_t* vs, int t) {
+    // S^T (64 keys x 32 queries) as two 32x32 blocks.
+    f32x16 s_acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s_acc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
+        s_acc[kb] = mfma32(a, qf[s], s_acc[kb]);
+        if (SPLIT_Q) s_acc[kb] = mfma32(a, ql[s], s_acc[kb]);
+      }
+    }
 
+    // Scores in the log2 domain; keys past n_keys get -inf.
+    float sv[2][16];
+    const int key0 = t * FWD_BC;
+    const bool partial = key0 + FWD_BC > n_keys;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float x;
+        if (POS_SCALE) x = s_acc[kb][j];
+        else x = s_acc[kb][j] * c2;
+        if (partial) {
+          const int key = key0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+          if (key >= n_keys) x = -INFINITY;
+        }
+        sv[kb][j] = x;
+      }
+    }
+    float mx = sv[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
+    mx = xor32_max(mx);
+    if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+
+    float psum = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float e;
+        if (POS_SCALE) e = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_new));
+        else e = __builtin_amdgcn_exp2f(sv[kb][j] - m_new);
+        pv[j] = e;
+        psum += e;
+      }
+      pf[2 * kb] = pack_acc8(pv);
+      pf[2 * kb + 1] = pack_acc8(pv + 8);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
+
+    // O^T (128 d x 32 queries) += V^T P^T over the 4 groups of 16 keys.
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const bf16x8 a = lds_col_frag(vs, kg * 16, d * 32, lane);
+        o_acc[d] = mfma32(a, pf[kg], o_acc[d]);
+      }
+    }
+
+  };
+
+  if (n_tiles > 0) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    tile_dma(smem[0][0], kbase, q_row_stride, 0, n_keys, wv, lane);
+    tile_dma(smem[0][1], vbase, q_row_stride, 0, n_keys, wv, lane);
+    wait_vmem();
+    __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
       const int buf = t & 1;
       const bool has_next = t + 1 < n_tiles;
       if (has_next) {
-        tile_load(kr, kbase, q_row_stride, (t + 1) * FWD_BC, n_keys, tid);
-        tile_load(vr, vbase, q_row_stride, (t + 1) * FWD_BC, n_keys, tid);
+        tile_dma(smem[buf ^ 1][0], kbase, q_row_stride, (t + 1) * FWD_BC, n_keys, wv, lane);
+        tile_dma(smem[buf ^ 1][1], vbase, q_row_stride, (t + 1) * FWD_BC, n_keys, wv, lane);
       }
-      const uint16_t* ks = smem[buf][0];
-      const uint16_t* vs = smem[buf][1];
-
-      // S^T (64 keys x 32 queries) as two 32x32 blocks.
-      f32x16 s_acc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s_acc[kb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
-          s_acc[kb] = mfma32(a, qf[s], s_acc[kb]);
-        }
-      }
-
-      // Scores in the log2 domain; keys past n_keys get -inf.
-      float sv[2][16];
-      const int key0 = t * FWD_BC;
-      const bool partial = key0 + FWD_BC > n_keys;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float x;
-          if (POS_SCALE) x = s_acc[kb][j];
-          else x = s_acc[kb][j] * c2;
-          if (partial) {
-            const int key = key0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (key >= n_keys) x = -INFINITY;
-          }
-          sv[kb][j] = x;
-        }
-      }
-      float mx = sv[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
-      mx = xor32_max(mx);
-      if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-
-      float psum = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float pv[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float e;
-          if (POS_SCALE) e = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_new));
-          else e = __builtin_amdgcn_exp2f(sv[kb][j] - m_new);
-          pv[j] = e;
-          psum += e;
-        }
-        pf[2 * kb] = pack_acc8(pv);
-        pf[2 * kb + 1] = pack_acc8(pv + 8);
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
-
-      // O^T (128 d x 32 queries) += V^T P^T over the 4 groups of 16 keys.
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-#pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-          const bf16x8 a = lds_col_frag(vs, kg * 16, d * 32, lane);
-          o_acc[d] = mfma32(a, pf[kg], o_acc[d]);
-        }
-      }
-
-      if (has_next) {
-        tile_store(smem[buf ^ 1][0], kr, tid);
-        tile_store(smem[buf ^ 1][1], vr, tid);
-      }
+      tile_step(smem[buf][0], smem[buf][1], t);
+      if (has_next) wait_vmem();
       __syncthreads();
     }
   }
@@ -211,10 +217,14 @@ hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)q.n_qtiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total), block(256);
+  // With RoPE the rotated query is carried as a bf16 hi + lo pair (see SPLIT_Q).
+  const bool split = p.rope.table != nullptr;
   if (p.scale_log2 > 0.f) {
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, block, 0, stream, q);
+    if (split) hipLaunchKernelGGL((attn_fwd_kernel<true, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((attn_fwd_kernel<true, false>), grid, block, 0, stream, q);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, block, 0, stream, q);
+    if (split) hipLaunchKernelGGL((attn_fwd_kernel<false, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((attn_fwd_kernel<false, false>), grid, block, 0, stream, q);
   }
   return hipGetLastError();
 }

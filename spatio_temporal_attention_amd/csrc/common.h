@@ -97,6 +97,23 @@ __device__ __forceinline__ u32x4 rope_chunk(const RopeDev& r, const TokenPos& p,
   return y;
 }
 
+// Same rotation, but the result is returned as a bf16 pair hi + lo with
+// hi = RNE(y) and lo = RNE(y - hi): together they carry ~16 significant bits,
+// so a product with them loses no more than a product with unrounded y would
+// to the second operand's own rounding.
+__device__ __forceinline__ void rope_chunk_split(const RopeDev& r, const TokenPos& p, int c, u32x4 x,
+                                                 u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float x0 = bf16_lo(x[t]);
+    float x1 = bf16_hi(x[t]);
+    rope_rotate(x0, x1, rope_cs(r, p, 4 * c + t), false);
+    const uint32_t h = pack_bf16(x0, x1);
+    hi[t] = h;
+    lo[t] = pack_bf16(x0 - bf16_lo(h), x1 - bf16_hi(h));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LDS tiles: 64 rows x 128 bf16, row-major, 256 bytes per row, no padding.
 // The 16 chunks (16 bytes each) of row r are stored at chunk c ^ swz(r).
@@ -157,6 +174,29 @@ __device__ __forceinline__ void tile_store(uint16_t* lds, const TileRegs& t, int
     *reinterpret_cast<u32x4*>(lds + tile_off(row, c * 8)) = t.r[i];
   }
 }
+
+// Direct global -> LDS staging of a 64-row tile by 4 waves (no registers):
+// wave w fills rows 16w .. 16w+15 with four 1 KB global_load_lds_dwordx4
+// instructions; lane l of an instruction lands at LDS byte 16*l of its 1 KB
+// block, i.e. row 16w + 4i + l/16, physical chunk l%16, so it fetches the
+// logical chunk (l%16) ^ swz(row).  Rows at or past `nrows` fetch row
+// nrows-1 instead (always valid data; callers mask those rows out), so no
+// padded or out-of-range memory is read.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void tile_dma(uint16_t* lds_tile, const uint16_t* base, int64_t row_stride, int row0,
+                                         int nrows, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rblk = 16 * wave + 4 * i;
+    const int r = rblk + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    const int grow = min(row0 + r, nrows - 1);
+    const uint16_t* src = base + (int64_t)grow * row_stride + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_tile + rblk * HD), 16, 0, 0);
+  }
+}
+
+// Wait for this wave's outstanding global (and LDS-DMA) loads.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // 16-byte row fragment: elements [8*chunk, 8*chunk+8) of `row`.
 __device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t* lds, int row, int chunk) {

@@ -24,7 +24,8 @@ struct FwdParams {
 
 // Self-attention backward.  All [B, L, H, 128] bf16 except lse/delta [B, H, L] fp32.
 struct BwdParams {
-  const uint16_t* q;        // rotated queries
+  const uint16_t* q;        // rotated queries (bf16 hi part when q_lo != nullptr)
+  const uint16_t* q_lo;     // rotated queries, lo part (q - hi rounded to bf16), or nullptr
   const uint16_t* k;        // rotated keys
   const uint16_t* v;
   const uint16_t* o;
@@ -45,6 +46,8 @@ hipError_t launch_rope_table(float* table, int f, int h, int w, int d_f, int d_h
                              hipStream_t stream);
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int B, int L, int H, const RopeDev& rope,
                          bool inverse, hipStream_t stream);
+hipError_t launch_rope3d_split(const uint16_t* x, uint16_t* hi, uint16_t* lo, int B, int L, int H,
+                               const RopeDev& rope, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_delta(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);

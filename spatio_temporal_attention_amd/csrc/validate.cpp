@@ -52,7 +52,7 @@ size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
   size_t delta = (size_t)B * H * L * 4;
   delta = (delta + 255) & ~(size_t)255;
   if (!with_rope) return delta;
-  return delta + 2 * (size_t)B * L * H * D * 2;   // + rotated queries and keys
+  return delta + 3 * (size_t)B * L * H * D * 2;   // + rotated queries (hi, lo) and keys
 }
 
 static int check_bf16(const void* p) {

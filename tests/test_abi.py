@@ -65,7 +65,7 @@ def test_workspace_sizes(lib):
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 0
     delta = (B * H * L * 4 + 255) // 256 * 256
     assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 2 * B * L * H * D * 2
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 3 * B * L * H * D * 2
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, 64, 1) == 0
 
 

