@@ -21,9 +21,12 @@
 //    flight while the current one is multiplied;
 //  * O^T += V^T P^T reads V through the LDS transpose read and takes P
 //    straight from the S^T accumulator registers (bf16, RNE);
-//  * online softmax in fp32 in the log2 domain (scale * log2 e folded in);
+//  * online softmax in fp32 in the log2 domain (scale * log2 e folded in),
+//    with lazy rescaling of O and l (only when a row max grows by > 2^8);
 //  * workgroups are ordered head-major and XCD-aware so that the resident
 //    workgroups of one XCD walk the same head's K/V through its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +37,7 @@ namespace {
 constexpr int FWD_WAVES = 4;
 constexpr int FWD_BR = 32 * FWD_WAVES;   // query rows per workgroup
 constexpr int FWD_BC = TILE_ROWS;         // keys per tile
+constexpr float RESCALE_SLACK = 8.0f;     // log2 units: P stays <= 256 between rescales
 
 template <bool POS_SCALE, bool SPLIT_Q>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
@@ -91,8 +95,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 
-  // One 64-key tile: scores, online softmax, O += P V.
-  auto tile_step = [&](const uint16_t* ks, const uint16_t* vs, int t) {
+  // One 64-key tile: scores, online softmax, O += P V.  MASK: the last tile,
+  // whose keys past n_keys get -inf (full tiles carry no masking code).
+  auto tile_step = [&](auto mask_tag, const uint16_t* ks, const uint16_t* vs, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // S^T (64 keys x 32 queries) as two 32x32 blocks.
     f32x16 s_acc[2];
 #pragma unroll
@@ -106,19 +112,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
 
-    // Scores in the log2 domain; keys past n_keys get -inf.
+    // Scores (raw for a positive scale, otherwise already in the log2 domain).
     float sv[2][16];
-    const int key0 = t * FWD_BC;
-    const bool partial = key0 + FWD_BC > n_keys;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x;
-        if (POS_SCALE) x = s_acc[kb][j];
-        else x = s_acc[kb][j] * c2;
-        if (partial) {
-          const int key = key0 + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        float x = POS_SCALE ? s_acc[kb][j] : s_acc[kb][j] * c2;
+        if (MASK) {
+          const int key = t * FWD_BC + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
           if (key >= n_keys) x = -INFINITY;
         }
         sv[kb][j] = x;
@@ -131,9 +133,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
     mx = xor32_max(mx);
     if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+
+    // Lazy rescaling: the running max only moves when some row's tile max
+    // exceeds it by more than RESCALE_SLACK (log2 units), so p <= 2^SLACK and
+    // the O/l rescale is skipped on almost every tile.  Exact either way: the
+    // final O / l and LSE = m + log2 l use the max that was applied.
+    if (__any(mx > m_run + RESCALE_SLACK)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
+    }
 
     float psum = 0.f;
     bf16x8 pf[4];
@@ -143,17 +155,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         float e;
-        if (POS_SCALE) e = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_new));
-        else e = __builtin_amdgcn_exp2f(sv[kb][j] - m_new);
+        if (POS_SCALE) e = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
+        else e = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
         pv[j] = e;
         psum += e;
       }
       pf[2 * kb] = pack_acc8(pv);
       pf[2 * kb + 1] = pack_acc8(pv + 8);
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
+    l_run += psum;
 
     // O^T (128 d x 32 queries) += V^T P^T over the 4 groups of 16 keys.
 #pragma unroll
@@ -164,7 +174,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
         o_acc[d] = mfma32(a, pf[kg], o_acc[d]);
       }
     }
-
   };
 
   if (n_tiles > 0) {
@@ -173,17 +182,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     tile_dma(smem[0][1], vbase, q_row_stride, 0, n_keys, wv, lane);
     wait_vmem();
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
+    // Full tiles in the loop; a partial last tile is peeled off after it.
+    const int n_full = n_keys / FWD_BC;
+    for (int t = 0; t < n_full; ++t) {
       const int buf = t & 1;
       const bool has_next = t + 1 < n_tiles;
       if (has_next) {
         tile_dma(smem[buf ^ 1][0], kbase, q_row_stride, (t + 1) * FWD_BC, n_keys, wv, lane);
         tile_dma(smem[buf ^ 1][1], vbase, q_row_stride, (t + 1) * FWD_BC, n_keys, wv, lane);
       }
-      tile_step(smem[buf][0], smem[buf][1], t);
+      tile_step(std::false_type{}, smem[buf][0], smem[buf][1], t);
       if (has_next) wait_vmem();
       __syncthreads();
     }
+    if (n_full < n_tiles) tile_step(std::true_type{}, smem[n_full & 1][0], smem[n_full & 1][1], n_full);
   }
 
   // ---- epilogue: O = O / l (bf16), LSE = ln sum exp(s) = ln2 * (m + log2 l)
