@@ -117,12 +117,16 @@ __device__ __forceinline__ void rope_chunk_split(const RopeDev& r, const TokenPo
 // ---------------------------------------------------------------------------
 // LDS tiles: 64 rows x 128 bf16, row-major, 256 bytes per row, no padding.
 // The 16 chunks (16 bytes each) of row r are stored at chunk c ^ swz(r).
-// swz permutes 0..15 so that (a) 8 consecutive rows read at one logical chunk
-// hit 8 distinct bank groups (16-byte row fragments), and (b) the 4 rows x
-// 32 bytes read by each 16-lane group of a transpose read do as well.
+// LDS has 64 banks of 4 bytes, so a row spans all banks once and a chunk's
+// bank group is its physical index.  swz(r) = ((r&3) << 2) | ((r>>2)&3):
+//  (a) 16 consecutive rows read at one logical chunk (16-byte row fragments,
+//      16 lanes per LDS cycle) land on 16 distinct chunks;
+//  (b) a 32-lane pass of the transpose read covers 4 rows 4m+e (e = 0..3) x
+//      4 aligned logical chunks; bits 2-3 of swz differ across e, so the rows
+//      land on 4 disjoint aligned chunk groups.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz(int r) {
-  return (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8)) & 15;
+  return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 // Offset (in bf16 elements) of element (row, col) inside a tile; col % 8 kept.
@@ -198,6 +202,16 @@ __device__ __forceinline__ void tile_dma(uint16_t* lds_tile, const uint16_t* bas
 // Wait for this wave's outstanding global (and LDS-DMA) loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier ordering LDS accesses only.  Unlike __syncthreads() it
+// does not wait for the wave's outstanding global loads (and so not for LDS
+// DMA in flight); callers wait for those explicitly with wait_vmem() before
+// the barrier that publishes them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 16-byte row fragment: elements [8*chunk, 8*chunk+8) of `row`.
 __device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t* lds, int row, int chunk) {
   return *reinterpret_cast<const bf16x8*>(lds + tile_off(row, chunk * 8));
@@ -244,12 +258,18 @@ __device__ __forceinline__ bf16x8 pack_acc8(const float* v) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Butterfly across the two 32-lane halves of the wave.
+// Butterfly across the two 32-lane halves of the wave (v_permlane32_swap:
+// after swapping a register with itself, the two results hold the lower and
+// the upper half's value in every lane).
 __device__ __forceinline__ float xor32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const uint32_t u = __float_as_uint(x);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
-  return x + __shfl_xor(x, 32);
+  const uint32_t u = __float_as_uint(x);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 // XCD-aware workgroup order: the hardware deals workgroups round-robin over
