@@ -28,6 +28,23 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_720p_hbm_traffic.json")
+FWD_SOURCES = ("attn_fwd.hip", "common.h", "kernels.h")
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE passes,
+    or None when the kernel sources have changed since they were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_PROFILE))
+    except (OSError, ValueError):
+        return None
+    csrc = os.path.join(ROOT, "spatio_temporal_attention_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, n), "rb").read() for n in FWD_SOURCES)
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return rec["traffic_bytes"]
 
 
 def parse():
@@ -201,7 +218,8 @@ def main():
                    "step": "self_fwd + cross_fwd + self_bwd" if not args.fwd_only else "self_fwd"},
         "pct_bf16_peak": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
                      "kernel": "attn_fwd_kernel (+ key pre-rotation inside the same timed call)",
                      "flop_per_launch": fwd_flop},
     }

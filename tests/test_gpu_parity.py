@@ -169,6 +169,11 @@ def test_self_fwd_720p_sampled():
     _sampled_self_fwd_check(4)
 
 
+def test_self_fwd_long_sampled():
+    """Grid 64x64x64 = 262144 tokens, 40 heads: 64 seeded rows per head."""
+    _sampled_self_fwd_check(5)
+
+
 # ---------------------------------------------------------------------------
 # Cross-attention forward
 # ---------------------------------------------------------------------------
