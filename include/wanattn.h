@@ -34,8 +34,10 @@
  *  Rounding.  All arithmetic is fp32 (MFMA accumulates bf16 products in fp32);
  *    every fp32 -> bf16 rounding is round-to-nearest-even.  Rotated keys are
  *    rounded to bf16 before the score products; a rotated query is carried as
- *    a bf16 pair hi + lo (hi = RNE(x), lo = RNE(x - hi)), so scores lose
- *    precision only to the keys' rounding.
+ *    hi + lo (hi = RNE_bf16(x); lo = x - hi, which the forward multiplies in
+ *    fp8 e4m3 after a per-row power-of-two scaling against an fp8 copy of the
+ *    rotated keys, and the backward in bf16), so scores lose precision mainly
+ *    to the keys' bf16 rounding.
  *  Memory.  Every pointer is device memory owned by the caller, which keeps it
  *    alive until the stream's work has finished.  bf16 buffers, the rope table
  *    and workspaces must be 16-byte aligned; fp32 and int32 buffers 4-byte
@@ -119,8 +121,13 @@ int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D,
  *   O_i  = sum_j exp(s_ij - LSE_i) v_j.
  * table == NULL: no rotation (g and r are then ignored).
  * lse may be NULL (not written).  scale: any finite value (1/sqrt(D) usual).
- * Workspace: with a table, ws must hold wanattn_self_fwd_workspace_bytes bytes
- * (the rotated keys, bf16 [B, L, H, D]); without one it is unused (may be NULL).
+ * Workspace (required, 16-byte aligned): wanattn_self_fwd_workspace_bytes(B, L,
+ * H, D, table != NULL) bytes.  It receives V transposed into 64-key tiles
+ * (bf16 [B, H, ceil(L/64), D, 64], zero-padded: the PV product's operand
+ * layout) and, with a table, the rotated keys as bf16 [B, L, H, D] and again
+ * as fp8 e4m3 [B, L, H, D] (the fp8 copy serves the low-order part of the
+ * rotated query's hi + lo split); each part starts on a 256-byte boundary.
+ * Its contents on return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 

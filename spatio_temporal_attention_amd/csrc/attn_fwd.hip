@@ -12,15 +12,22 @@
 //  * each wave keeps its 32 rotated query rows in registers as the B operand
 //    of S^T = K Q^T (bf16 MFMA 32x32x16), so every lane owns one query row and
 //    the softmax needs one cross-lane step (lane l <-> l^32) per tile;
-//  * SPLIT_Q (with RoPE): the rotated query is held as bf16 hi + lo and S^T
-//    takes two MFMAs per step.  A single bf16 rounding of the rotated query
-//    moves LSE by up to ~1.2e-3 at 720p (tail of the row distribution); with
-//    the pair the error is set by the keys' rounding alone (~5e-5);
+//  * SPLIT_Q (with RoPE): the rotated query is carried as hi + lo, hi =
+//    RNE_bf16(q~) and lo = q~ - hi.  A single bf16 rounding of the rotated
+//    query moves LSE by up to ~1.2e-3 at 720p (tail of the row distribution).
+//    lo is ~2^-9 of q~, so its product needs few bits: it runs as a scaled
+//    fp8 MFMA (32x32x64, e4m3, twice the bf16 rate) of lo * 2^e (per-row
+//    power of two, undone by the E8M0 scale operand) against an fp8 copy of
+//    the rotated keys; the score error is then set by the keys' bf16 rounding;
 //  * K and V tiles of 64 keys go global -> LDS directly (global_load_lds,
 //    row-major, swizzled), double-buffered: the next tile's loads are in
 //    flight while the current one is multiplied;
-//  * O^T += V^T P^T reads V through the LDS transpose read and takes P
-//    straight from the S^T accumulator registers (bf16, RNE);
+//  * O^T += V^T P^T takes P straight from the S^T accumulator registers
+//    (bf16, RNE).  Self-attention reads V from V^T tiles written by a
+//    pre-pass (v_tiles_kernel), one plain 16-byte LDS read per fragment; the
+//    LDS transpose read (ds_read_b64_tr_b16) moves under half as many bytes
+//    per clock and would make the loop LDS-bound.  Cross-attention (a short
+//    text context, no workspace) keeps the transpose read;
 //  * online softmax in fp32 in the log2 domain (scale * log2 e folded in),
 //    with lazy rescaling of O and l (only when a row max grows by > 2^8);
 //  * workgroups are ordered head-major and XCD-aware so that the resident
@@ -39,9 +46,10 @@ constexpr int FWD_BR = 32 * FWD_WAVES;   // query rows per workgroup
 constexpr int FWD_BC = TILE_ROWS;         // keys per tile
 constexpr float RESCALE_SLACK = 8.0f;     // log2 units: P stays <= 256 between rescales
 
-template <bool POS_SCALE, bool SPLIT_Q>
+template <bool POS_SCALE, bool SPLIT_Q, bool TILED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE_ELEMS];   // [buffer][K|V]
+  __shared__ __attribute__((aligned(16))) uint8_t k8mem[SPLIT_Q ? 2 : 1][SPLIT_Q ? TILE_ELEMS : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -62,27 +70,74 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   const uint16_t* qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * HD;
   const uint16_t* kbase = p.k + ((int64_t)b * p.Lk * p.H + h) * HD;
   const uint16_t* vbase = p.v + ((int64_t)b * p.Lk * p.H + h) * HD;
+  // Tiled keys/values (self-attention): tile t of (b, h) is contiguous.
+  const int64_t tile0 = (int64_t)(b * p.H + h) * ((p.Lk + FWD_BC - 1) / FWD_BC);
+  const uint16_t* kt = TILED ? p.kt + tile0 * TILE_ELEMS : nullptr;
+  const uint16_t* vt = TILED ? p.vt + tile0 * TILE_ELEMS : nullptr;
+  const uint8_t* k8t = SPLIT_Q ? p.k8t + tile0 * TILE_ELEMS : nullptr;
 
   // ---- query fragments (B operand of S^T = K Q^T): lane holds row i, d in [16s + 8*half, +8)
   const int i = qt * FWD_BR + wave * 32 + col;
   const bool row_ok = i < p.Lq;
   bf16x8 qf[8];
-  bf16x8 ql[SPLIT_Q ? 8 : 1];
+  i32x8 ql8[SPLIT_Q ? 2 : 1];   // low-order part of the rotated query, fp8, B layout of 32x32x64
+  int q_scale = 127;            // E8M0 scale undoing the per-row power of two applied to ql8
   {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      u32x4 xl = u32x4{0u, 0u, 0u, 0u};
       const int c = 2 * s + half;
       if (row_ok) {
         x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
-        if (SPLIT_Q) rope_chunk_split(p.rope, pos, c, x, x, xl);
-        else if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
+        if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
       }
       qf[s] = __builtin_bit_cast(bf16x8, x);
-      if (SPLIT_Q) ql[s] = __builtin_bit_cast(bf16x8, xl);
+    }
+    if (SPLIT_Q) {
+      // lo = rotated q - RNE_bf16(rotated q) for head dims [64 ks + 32 half, +32),
+      // scaled by 2^e so the row's largest |lo| lands in [128, 256), as fp8.
+      float lo[2][32];
+      float mlo = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int c = 8 * ks + 4 * half + cc;
+          u32x4 x = u32x4{0u, 0u, 0u, 0u};
+          if (row_ok) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float x0 = bf16_lo(x[t]);
+            float x1 = bf16_hi(x[t]);
+            if (row_ok) rope_rotate(x0, x1, rope_cs(p.rope, pos, 4 * c + t), false);
+            const uint32_t hb = pack_bf16(x0, x1);
+            const float l0 = x0 - bf16_lo(hb);
+            const float l1 = x1 - bf16_hi(hb);
+            lo[ks][8 * cc + 2 * t] = l0;
+            lo[ks][8 * cc + 2 * t + 1] = l1;
+            mlo = fmaxf(mlo, fmaxf(fabsf(l0), fabsf(l1)));
+          }
+        }
+      }
+      mlo = xor32_max(mlo);
+      int e = 0;
+      if (mlo > 0.f) {
+        int ex;
+        frexpf(mlo, &ex);         // mlo = f * 2^ex, f in [0.5, 1)
+        e = min(max(8 - ex, -100), 100);
+      }
+      q_scale = 127 - e;
+      const float sc = ldexpf(1.f, e);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          ql8[ks][w] = (int)pack_fp8x4(lo[ks][4 * w] * sc, lo[ks][4 * w + 1] * sc, lo[ks][4 * w + 2] * sc,
+                                       lo[ks][4 * w + 3] * sc);
+        }
+      }
     }
   }
 
@@ -97,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   // One 64-key tile: scores, online softmax, O += P V.  MASK: the last tile,
   // whose keys past n_keys get -inf (full tiles carry no masking code).
-  auto tile_step = [&](auto mask_tag, const uint16_t* ks, const uint16_t* vs, int t) {
+  auto tile_step = [&](auto mask_tag, const uint16_t* ks, const uint16_t* vs, const uint8_t* k8s, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // S^T (64 keys x 32 queries) as two 32x32 blocks.
     f32x16 s_acc[2];
@@ -108,7 +163,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       for (int s = 0; s < 8; ++s) {
         const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
         s_acc[kb] = mfma32(a, qf[s], s_acc[kb]);
-        if (SPLIT_Q) s_acc[kb] = mfma32(a, ql[s], s_acc[kb]);
+      }
+      if (SPLIT_Q) {
+        // + fp8 keys x fp8 low-order query, the row's 2^e undone by the MFMA scale
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const i32x8 a8 = lds_row_frag8(k8s, kb * 32 + col, k2, half);
+          s_acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, ql8[k2], s_acc[kb], 0, 0, 0, 127, 0,
+                                                                     q_scale);
+        }
       }
     }
 
@@ -147,6 +210,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
     }
 
+    // P in bf16 (RNE) for PV; l sums P in fp32 (summing the rounded values
+    // instead would move LSE by up to ~2^-9 when few keys dominate).
     float psum = 0.f;
     bf16x8 pf[4];
 #pragma unroll
@@ -154,11 +219,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       float pv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float e;
-        if (POS_SCALE) e = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
-        else e = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
-        pv[j] = e;
-        psum += e;
+        if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
+        else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
+        psum += pv[j];
       }
       pf[2 * kb] = pack_acc8(pv);
       pf[2 * kb + 1] = pack_acc8(pv + 8);
@@ -170,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg) {
-        const bf16x8 a = lds_col_frag(vs, kg * 16, d * 32, lane);
+        const bf16x8 a = TILED ? lds_vt_frag(vs, d * 32 + col, kg, half) : lds_col_frag(vs, kg * 16, d * 32, lane);
         o_acc[d] = mfma32(a, pf[kg], o_acc[d]);
       }
     }
@@ -178,8 +241,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   if (n_tiles > 0) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    tile_dma(smem[0][0], kbase, q_row_stride, 0, n_keys, wv, lane);
-    tile_dma(smem[0][1], vbase, q_row_stride, 0, n_keys, wv, lane);
+    // Stage tile t of K (bf16, and fp8 with SPLIT_Q) and V into buffer `buf`.
+    auto stage = [&](int buf, int t) {
+      if (TILED) {
+        ktile_dma(smem[buf][0], kt + (int64_t)t * TILE_ELEMS, wv, lane);
+        rows128_tile_dma<4>(reinterpret_cast<uint8_t*>(smem[buf][1]),
+                            reinterpret_cast<const uint8_t*>(vt + (int64_t)t * TILE_ELEMS), wv, lane);
+        if (SPLIT_Q) rows128_tile_dma<2>(k8mem[buf], k8t + (int64_t)t * TILE_ELEMS, wv, lane);
+      } else {
+        tile_dma(smem[buf][0], kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
+        tile_dma(smem[buf][1], vbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
+      }
+    };
+    stage(0, 0);
     wait_vmem();
     __syncthreads();
     // Full tiles in the loop; a partial last tile is peeled off after it.
@@ -187,15 +261,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     for (int t = 0; t < n_full; ++t) {
       const int buf = t & 1;
       const bool has_next = t + 1 < n_tiles;
-      if (has_next) {
-        tile_dma(smem[buf ^ 1][0], kbase, q_row_stride, (t + 1) * FWD_BC, n_keys, wv, lane);
-        tile_dma(smem[buf ^ 1][1], vbase, q_row_stride, (t + 1) * FWD_BC, n_keys, wv, lane);
-      }
-      tile_step(std::false_type{}, smem[buf][0], smem[buf][1], t);
+      if (has_next) stage(buf ^ 1, t + 1);
+      tile_step(std::false_type{}, smem[buf][0], smem[buf][1], k8mem[SPLIT_Q ? buf : 0], t);
       if (has_next) wait_vmem();
       __syncthreads();
     }
-    if (n_full < n_tiles) tile_step(std::true_type{}, smem[n_full & 1][0], smem[n_full & 1][1], n_full);
+    if (n_full < n_tiles)
+      tile_step(std::true_type{}, smem[n_full & 1][0], smem[n_full & 1][1], k8mem[SPLIT_Q ? (n_full & 1) : 0], n_full);
   }
 
   // ---- epilogue: O = O / l (bf16), LSE = ln sum exp(s) = ln2 * (m + log2 l)
@@ -229,14 +301,20 @@ hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)q.n_qtiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total), block(256);
-  // With RoPE the rotated query is carried as a bf16 hi + lo pair (see SPLIT_Q).
+  // With RoPE the rotated query is carried as bf16 hi + fp8 lo (see SPLIT_Q),
+  // which needs the tiled fp8 copy of the rotated keys (self-attention only).
   const bool split = p.rope.table != nullptr;
+  const bool vt = p.kt != nullptr;
+  if (vt && (p.vt == nullptr || p.k_lens != nullptr || p.Lk != p.Lq)) return hipErrorInvalidValue;
+  if (split && (p.k8t == nullptr || !vt)) return hipErrorInvalidValue;
   if (p.scale_log2 > 0.f) {
-    if (split) hipLaunchKernelGGL((attn_fwd_kernel<true, true>), grid, block, 0, stream, q);
-    else hipLaunchKernelGGL((attn_fwd_kernel<true, false>), grid, block, 0, stream, q);
+    if (split) hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, q);
+    else if (vt) hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((attn_fwd_kernel<true, false, false>), grid, block, 0, stream, q);
   } else {
-    if (split) hipLaunchKernelGGL((attn_fwd_kernel<false, true>), grid, block, 0, stream, q);
-    else hipLaunchKernelGGL((attn_fwd_kernel<false, false>), grid, block, 0, stream, q);
+    if (split) hipLaunchKernelGGL((attn_fwd_kernel<false, true, true>), grid, block, 0, stream, q);
+    else if (vt) hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((attn_fwd_kernel<false, false, false>), grid, block, 0, stream, q);
   }
   return hipGetLastError();
 }

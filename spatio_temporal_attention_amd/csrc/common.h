@@ -26,6 +26,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ---------------------------------------------------------------------------
@@ -39,6 +40,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   f32x2 v = {a, b};
   bf16x2 p = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Four fp32 -> packed OCP fp8 e4m3 (round to nearest even), saturated to +-448
+// so that out-of-range values never become NaN.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  constexpr float M = 448.f;
+  a = fminf(fmaxf(a, -M), M);
+  b = fminf(fmaxf(b, -M), M);
+  c = fminf(fmaxf(c, -M), M);
+  d = fminf(fmaxf(d, -M), M);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -134,51 +147,6 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
-// Global -> register staging of a 64-row tile: thread t (of 256) owns rows
-// 4*(t/16) + i, i = 0..3, at 16-byte column chunk t%16.  Each 16-lane group of
-// a load instruction reads one whole 256-byte row (coalesced).  Rows >= nrows
-// are zero and never read from memory.
-struct TileRegs {
-  u32x4 r[4];
-};
-
-__device__ __forceinline__ void tile_load(TileRegs& t, const uint16_t* base, int64_t row_stride,
-                                          int row0, int nrows, int tid) {
-  const int c = tid & 15;
-  const int rq = (tid >> 4) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rq + i;
-    if (row0 + row < nrows) {
-      t.r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)(row0 + row) * row_stride + c * 8);
-    } else {
-      t.r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-// Optional RoPE on the staged rows (tokens row0 + row).
-__device__ __forceinline__ void tile_rope(TileRegs& t, const RopeDev& rd, int row0, int nrows, int tid,
-                                          bool inverse) {
-  const int c = tid & 15;
-  const int rq = (tid >> 4) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = row0 + rq + i;
-    if (n < nrows) t.r[i] = rope_chunk(rd, token_pos(rd, n), c, t.r[i], inverse);
-  }
-}
-
-__device__ __forceinline__ void tile_store(uint16_t* lds, const TileRegs& t, int tid) {
-  const int c = tid & 15;
-  const int rq = (tid >> 4) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rq + i;
-    *reinterpret_cast<u32x4*>(lds + tile_off(row, c * 8)) = t.r[i];
-  }
-}
-
 // Direct global -> LDS staging of a 64-row tile by 4 waves (no registers):
 // wave w fills rows 16w .. 16w+15 with four 1 KB global_load_lds_dwordx4
 // instructions; lane l of an instruction lands at LDS byte 16*l of its 1 KB
@@ -199,6 +167,19 @@ __device__ __forceinline__ void tile_dma(uint16_t* lds_tile, const uint16_t* bas
   }
 }
 
+// The same staging from one contiguous 64 x 128 bf16 tile (rows 256 bytes
+// apart, all present): the per-lane offsets do not depend on the tile.
+__device__ __forceinline__ void ktile_dma(uint16_t* lds_tile, const uint16_t* tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rblk = 16 * wave + 4 * i;
+    const int r = rblk + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    __builtin_amdgcn_global_load_lds(tile + r * HD + c * 8,
+                                     (__attribute__((address_space(3))) void*)(lds_tile + rblk * HD), 16, 0, 0);
+  }
+}
+
 // Wait for this wave's outstanding global (and LDS-DMA) loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -210,6 +191,47 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Tiles of 128-byte rows: the fp8 key tile (64 keys x 128 d, 8 KB) and the
+// V^T tile (128 d x 64 keys in bf16, 16 KB).  The 8 16-byte chunks of row r
+// sit at chunk c ^ swz8(r), swz8(r) = (r >> 1) & 7: the 16 rows a 16-lane
+// pass reads at one logical chunk (two rows per 256-byte bank cycle) land on
+// 16 distinct bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int tile8_off(int row, int chunk) { return row * 128 + ((chunk ^ swz8(row)) << 4); }
+
+// Direct global -> LDS staging of a contiguous tile of 128-byte rows by 4
+// waves: wave w fills rows [8*NI*w, 8*NI*(w+1)), one 1 KB instruction per 8
+// rows; lane l lands at byte 16*l of its block (row rblk + l/8, physical
+// chunk l%8) and so fetches logical chunk (l%8) ^ swz8(row).
+// NI = 2: the fp8 key tile (64 x 128 bytes); NI = 4: the V^T tile (128 x 64 bf16).
+template <int NI>
+__device__ __forceinline__ void rows128_tile_dma(uint8_t* lds_tile, const uint8_t* tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int rblk = 8 * NI * wave + 8 * i;
+    const int r = rblk + (lane >> 3);
+    const int c = (lane & 7) ^ swz8(r);
+    __builtin_amdgcn_global_load_lds(tile + r * 128 + c * 16,
+                                     (__attribute__((address_space(3))) void*)(lds_tile + rblk * 128), 16, 0, 0);
+  }
+}
+
+// A-side fragment of O^T += V^T P^T from a V^T tile: lane l gets d-row `row`,
+// key positions [16*kg + 8*(l/32), +8).  Within each 16-key group the tile
+// stores key k at position k with bits 2 and 3 swapped, so these 8 positions
+// hold keys {16kg + 4*(l/32) + e, 16kg + 8 + 4*(l/32) + e : e = 0..3}: the k
+// order of a 32x32 accumulator block's registers (see mfma32 below).
+__device__ __forceinline__ bf16x8 lds_vt_frag(const uint16_t* lds, int row, int kg, int half) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(lds) + tile8_off(row, 2 * kg + half));
+}
+
+// fp8 MFMA 32x32x64 A-side fragment: lane l gets bytes [64*ks + 32*(l/32), +32) of `row`.
+__device__ __forceinline__ i32x8 lds_row_frag8(const uint8_t* lds, int row, int ks, int half) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + tile8_off(row, 4 * ks + 2 * half));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + tile8_off(row, 4 * ks + 2 * half + 1));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 // 16-byte row fragment: elements [8*chunk, 8*chunk+8) of `row`.

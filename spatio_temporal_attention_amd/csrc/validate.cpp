@@ -41,10 +41,24 @@ int64_t rope_table_entries(wanattn_grid g, wanattn_rope r) {
   return (int64_t)g.f * (r.d_f / 2) + (int64_t)g.h * (r.d_h / 2) + (int64_t)g.w * (r.d_w / 2);
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
+  FwdWsLayout w{0, 0, 0, 0};
+  if (check_dims(B, L, H, D) != WANATTN_OK) return w;
+  const size_t tile_elems = (size_t)B * H * (((size_t)L + 63) / 64) * 64 * (size_t)D;
+  w.kt = 0;                                   // K~ tiles [B, H, tile, 64, D] bf16
+  w.vt = align256(tile_elems * 2);            // V^T tiles [B, H, tile, D, 64] bf16
+  w.total = align256(w.vt + tile_elems * 2);
+  if (with_rope) {
+    w.k8t = w.total;                          // K~ tiles [B, H, tile, 64, D] fp8 e4m3
+    w.total = w.k8t + tile_elems;
+  }
+  return w;
+}
+
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
-  if (check_dims(B, L, H, D) != WANATTN_OK) return 0;
-  if (!with_rope) return 0;
-  return (size_t)B * L * H * D * 2;   // rotated keys
+  return self_fwd_ws_layout(B, L, H, D, with_rope).total;
 }
 
 size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
@@ -87,11 +101,9 @@ int validate_self_fwd(const void* q, const void* k, const void* v, const void* o
   WANATTN_TRY(check_bf16(v));
   WANATTN_TRY(check_bf16(o));
   if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
-  if (table != nullptr) {
-    if (!aligned(table, 16)) return WANATTN_ERR_ALIGN;
-    if (ws == nullptr || ws_bytes < self_fwd_ws_bytes(B, L, H, D, 1)) return WANATTN_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
-  }
+  if (table != nullptr && !aligned(table, 16)) return WANATTN_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < self_fwd_ws_bytes(B, L, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
   return WANATTN_OK;
 }
 

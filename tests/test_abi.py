@@ -61,8 +61,12 @@ def test_rope_table_bytes(lib):
 
 def test_workspace_sizes(lib):
     B, L, H, D = 1, 75600, 40, 128
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == B * L * H * D * 2
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 0
+    n = B * L * H * D
+    tiled = B * H * ((L + 63) // 64) * 64 * D           # elements of K or V in 64-key tiles, zero-padded
+    assert tiled > n
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 2 * tiled * 2          # K~ and V^T, bf16
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + tiled  # + K~ in fp8
+    assert lib.wanattn_self_fwd_workspace_bytes(1, 1, 1, D, 0) == 2 * 64 * D * 2
     delta = (B * H * L * 4 + 255) // 256 * 256
     assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta
     assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 3 * B * L * H * D * 2
@@ -91,6 +95,11 @@ def test_self_fwd_validation(lib):
     assert _fwd(lib, table=ODD) == ALIGN
     assert _fwd(lib, ws=None) == WS
     assert _fwd(lib, ws_bytes=320 * 2 * 128 * 2 - 1) == WS
+    assert _fwd(lib, table=None, ws=None) == WS
+    need0 = lib.wanattn_self_fwd_workspace_bytes(1, 320, 2, 128, 0)
+    assert _fwd(lib, ws_bytes=lib.wanattn_self_fwd_workspace_bytes(1, 320, 2, 128, 1) - 1) == WS
+    assert _fwd(lib, table=None, ws_bytes=need0 - 1) == WS
+    assert _fwd(lib, table=None, ws=ODD, ws_bytes=need0, q=None) == NULL
     assert _fwd(lib, L=1 << 30, g=Grid(1 << 10, 1 << 10, 1 << 10), H=1 << 14) == SHAPE   # too large
 
 
