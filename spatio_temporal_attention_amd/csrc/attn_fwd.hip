@@ -71,10 +71,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + ((int64_t)b * p.Lk * p.H + h) * HD;
   const uint16_t* vbase = p.v + ((int64_t)b * p.Lk * p.H + h) * HD;
   // Tiled keys/values (self-attention): tile t of (b, h) is contiguous.
-  const int64_t tile0 = (int64_t)(b * p.H + h) * ((p.Lk + FWD_BC - 1) / FWD_BC);
-  const uint16_t* kt = TILED ? p.kt + tile0 * TILE_ELEMS : nullptr;
-  const uint16_t* vt = TILED ? p.vt + tile0 * TILE_ELEMS : nullptr;
-  const uint8_t* k8t = SPLIT_Q ? p.k8t + tile0 * TILE_ELEMS : nullptr;
+  const int nkt = (p.Lk + FWD_BC - 1) / FWD_BC;
+  const int64_t tile0 = (int64_t)(b * p.H + h) * nkt;
 
   // ---- query fragments (B operand of S^T = K Q^T): lane holds row i, d in [16s + 8*half, +8)
   const int i = qt * FWD_BR + wave * 32 + col;
@@ -85,19 +83,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
+    // With SPLIT_Q the query carries the softmax scale: q' = c2 * R(p) q in
+    // fp32 (c2 = scale * log2 e), so S = K q' is already in the log2 domain.
+    auto rotate_pair = [&](uint32_t w, int pair, float& y0, float& y1) {
+      y0 = bf16_lo(w);
+      y1 = bf16_hi(w);
+      rope_rotate(y0, y1, rope_cs(p.rope, pos, pair), false);
+      y0 *= p.scale_log2;
+      y1 *= p.scale_log2;
+    };
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 x = u32x4{0u, 0u, 0u, 0u};
       const int c = 2 * s + half;
       if (row_ok) {
         x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
-        if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
+        if (SPLIT_Q) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float y0, y1;
+            rotate_pair(x[t], 4 * c + t, y0, y1);
+            x[t] = pack_bf16(y0, y1);
+          }
+        } else if (p.rope.table != nullptr) {
+          x = rope_chunk(p.rope, pos, c, x, false);
+        }
       }
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
     if (SPLIT_Q) {
-      // lo = rotated q - RNE_bf16(rotated q) for head dims [64 ks + 32 half, +32),
-      // scaled by 2^e so the row's largest |lo| lands in [128, 256), as fp8.
+      // lo = q' - RNE_bf16(q') for head dims [64 ks + 32 half, +32), scaled
+      // by 2^e so the row's largest |lo| lands in [128, 256), as fp8.
       float lo[2][32];
       float mlo = 0.f;
 #pragma unroll
@@ -109,9 +125,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
           if (row_ok) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            float x0 = bf16_lo(x[t]);
-            float x1 = bf16_hi(x[t]);
-            if (row_ok) rope_rotate(x0, x1, rope_cs(p.rope, pos, 4 * c + t), false);
+            float x0 = 0.f, x1 = 0.f;
+            if (row_ok) rotate_pair(x[t], 4 * c + t, x0, x1);
             const uint32_t hb = pack_bf16(x0, x1);
             const float l0 = x0 - bf16_lo(hb);
             const float l1 = x1 - bf16_hi(hb);
@@ -147,6 +162,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   float m_run = -INFINITY;   // running max of scale*log2e*s (this lane's row)
   float l_run = 0.f;         // this lane's partial exp-sum (the other half holds the rest)
   const float c2 = p.scale_log2;
+  // SPLIT_Q: the score MFMAs start from -m_c (m_c = m_run once finite, 0
+  // before), so the accumulator holds S - m_c and P = exp2 of it directly.
+  float m_c = 0.f;
+  f32x16 neg_m = f32x16{};
 
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 
@@ -158,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     f32x16 s_acc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s_acc[kb] = f32x16{};
+      s_acc[kb] = SPLIT_Q ? neg_m : f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
@@ -175,13 +194,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
 
-    // Scores (raw for a positive scale, otherwise already in the log2 domain).
+    // Scores: SPLIT_Q S - m_c (log2 domain); else raw for a positive scale,
+    // otherwise already scaled to the log2 domain.
     float sv[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x = POS_SCALE ? s_acc[kb][j] : s_acc[kb][j] * c2;
+        float x = (SPLIT_Q || POS_SCALE) ? s_acc[kb][j] : s_acc[kb][j] * c2;
         if (MASK) {
           const int key = t * FWD_BC + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
           if (key >= n_keys) x = -INFINITY;
@@ -195,7 +215,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
     mx = xor32_max(mx);
-    if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
+    if (SPLIT_Q) mx += m_c;
+    else if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
 
     // Lazy rescaling: the running max only moves when some row's tile max
     // exceeds it by more than RESCALE_SLACK (log2 units), so p <= 2^SLACK and
@@ -208,6 +229,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
+      if (SPLIT_Q) {
+        const float delta = m_new - m_c;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sv[kb][j] -= delta;
+        m_c = m_new;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) neg_m[j] = -m_new;
+      }
     }
 
     // P in bf16 (RNE) for PV; l sums P in fp32 (summing the rounded values
@@ -219,7 +250,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       float pv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
+        if (SPLIT_Q) pv[j] = __builtin_amdgcn_exp2f(sv[kb][j]);
+        else if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
         else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
         psum += pv[j];
       }
@@ -241,13 +273,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   if (n_tiles > 0) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t koff[4], voff[4], k8off[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      koff[i] = ktile_lane_off(wv, i, lane);
+      voff[i] = rows128_lane_off<4>(wv, i, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) k8off[i] = rows128_lane_off<2>(wv, i, lane);
+    const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(TILED ? p.kt + tile0 * TILE_ELEMS : p.k, bytes);
+    const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(TILED ? p.vt + tile0 * TILE_ELEMS : p.v, bytes);
+    const __amdgpu_buffer_rsrc_t k8rs = tile_rsrc(SPLIT_Q ? p.k8t + tile0 * TILE_ELEMS : nullptr, bytes / 2);
     // Stage tile t of K (bf16, and fp8 with SPLIT_Q) and V into buffer `buf`.
     auto stage = [&](int buf, int t) {
       if (TILED) {
-        ktile_dma(smem[buf][0], kt + (int64_t)t * TILE_ELEMS, wv, lane);
-        rows128_tile_dma<4>(reinterpret_cast<uint8_t*>(smem[buf][1]),
-                            reinterpret_cast<const uint8_t*>(vt + (int64_t)t * TILE_ELEMS), wv, lane);
-        if (SPLIT_Q) rows128_tile_dma<2>(k8mem[buf], k8t + (int64_t)t * TILE_ELEMS, wv, lane);
+        const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+        uint8_t* kl = reinterpret_cast<uint8_t*>(smem[buf][0]) + 4096 * wv;
+        uint8_t* vl = reinterpret_cast<uint8_t*>(smem[buf][1]) + 4096 * wv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          buf_dma16(krs, koff[i], soff, kl + 1024 * i);
+          buf_dma16(vrs, voff[i], soff, vl + 1024 * i);
+        }
+        if (SPLIT_Q) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) buf_dma16(k8rs, k8off[i], soff / 2, k8mem[buf] + 2048 * wv + 1024 * i);
+        }
       } else {
         tile_dma(smem[buf][0], kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
         tile_dma(smem[buf][1], vbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
@@ -306,14 +358,18 @@ hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   const bool split = p.rope.table != nullptr;
   const bool vt = p.kt != nullptr;
   if (vt && (p.vt == nullptr || p.k_lens != nullptr || p.Lk != p.Lq)) return hipErrorInvalidValue;
+  // The tiles of one (b, h) are addressed through a buffer resource of 32-bit extent.
+  if (vt && (int64_t)((p.Lk + FWD_BC - 1) / FWD_BC) * (TILE_ELEMS * 2) > (int64_t)0xffffffff)
+    return hipErrorInvalidValue;
   if (split && (p.k8t == nullptr || !vt)) return hipErrorInvalidValue;
-  if (p.scale_log2 > 0.f) {
-    if (split) hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, q);
-    else if (vt) hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, q);
+  if (split) {
+    // The scale rides on the query (any sign).
+    hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, q);
+  } else if (p.scale_log2 > 0.f) {
+    if (vt) hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, q);
     else hipLaunchKernelGGL((attn_fwd_kernel<true, false, false>), grid, block, 0, stream, q);
   } else {
-    if (split) hipLaunchKernelGGL((attn_fwd_kernel<false, true, true>), grid, block, 0, stream, q);
-    else if (vt) hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, q);
+    if (vt) hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, q);
     else hipLaunchKernelGGL((attn_fwd_kernel<false, false, false>), grid, block, 0, stream, q);
   }
   return hipGetLastError();

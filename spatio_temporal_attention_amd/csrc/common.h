@@ -167,19 +167,6 @@ __device__ __forceinline__ void tile_dma(uint16_t* lds_tile, const uint16_t* bas
   }
 }
 
-// The same staging from one contiguous 64 x 128 bf16 tile (rows 256 bytes
-// apart, all present): the per-lane offsets do not depend on the tile.
-__device__ __forceinline__ void ktile_dma(uint16_t* lds_tile, const uint16_t* tile, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rblk = 16 * wave + 4 * i;
-    const int r = rblk + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
-    __builtin_amdgcn_global_load_lds(tile + r * HD + c * 8,
-                                     (__attribute__((address_space(3))) void*)(lds_tile + rblk * HD), 16, 0, 0);
-  }
-}
-
 // Wait for this wave's outstanding global (and LDS-DMA) loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -201,21 +188,32 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int tile8_off(int row, int chunk) { return row * 128 + ((chunk ^ swz8(row)) << 4); }
 
-// Direct global -> LDS staging of a contiguous tile of 128-byte rows by 4
-// waves: wave w fills rows [8*NI*w, 8*NI*(w+1)), one 1 KB instruction per 8
-// rows; lane l lands at byte 16*l of its block (row rblk + l/8, physical
-// chunk l%8) and so fetches logical chunk (l%8) ^ swz8(row).
-// NI = 2: the fp8 key tile (64 x 128 bytes); NI = 4: the V^T tile (128 x 64 bf16).
+// Staging from contiguous tiles (all rows present).  The per-lane byte
+// offsets do not depend on the tile, so they are computed once; lane l of a
+// 1 KB copy lands at byte 16*l of its LDS block.
+//   bf16 tile, 64 rows x 256 B, instruction i of wave w: rows 16w + 4i + l/16,
+//     logical chunk (l%16) ^ swz(row) (the layout of tile_dma);
+//   tile of 128-byte rows, instruction i of wave w with NI per wave: rows
+//     8*NI*w + 8i + l/8, logical chunk (l%8) ^ swz8(row).
+__device__ __forceinline__ uint32_t ktile_lane_off(int wave, int i, int lane) {
+  const int r = 16 * wave + 4 * i + (lane >> 4);
+  return (uint32_t)(r * 256 + (((lane & 15) ^ swz(r)) << 4));
+}
 template <int NI>
-__device__ __forceinline__ void rows128_tile_dma(uint8_t* lds_tile, const uint8_t* tile, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int rblk = 8 * NI * wave + 8 * i;
-    const int r = rblk + (lane >> 3);
-    const int c = (lane & 7) ^ swz8(r);
-    __builtin_amdgcn_global_load_lds(tile + r * 128 + c * 16,
-                                     (__attribute__((address_space(3))) void*)(lds_tile + rblk * 128), 16, 0, 0);
-  }
+__device__ __forceinline__ uint32_t rows128_lane_off(int wave, int i, int lane) {
+  const int r = 8 * NI * wave + 8 * i + (lane >> 3);
+  return (uint32_t)(r * 128 + (((lane & 7) ^ swz8(r)) << 4));
+}
+// Raw buffer resource over `bytes` bytes at `base` (stride 0; dword 3 as for
+// gfx9 raw buffers).  Copies through it keep the per-tile step in the scalar
+// soffset and the lane offset in a 32-bit voffset (buffer_load ... lds).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One 1 KB copy: 64 lanes x 16 bytes from base + soff + voff into lds_block.
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, soff, 0,
+                                           0);
 }
 
 // A-side fragment of O^T += V^T P^T from a V^T tile: lane l gets d-row `row`,
@@ -226,6 +224,7 @@ __device__ __forceinline__ void rows128_tile_dma(uint8_t* lds_tile, const uint8_
 __device__ __forceinline__ bf16x8 lds_vt_frag(const uint16_t* lds, int row, int kg, int half) {
   return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(lds) + tile8_off(row, 2 * kg + half));
 }
+
 
 // fp8 MFMA 32x32x64 A-side fragment: lane l gets bytes [64*ks + 32*(l/32), +32) of `row`.
 __device__ __forceinline__ i32x8 lds_row_frag8(const uint8_t* lds, int row, int ks, int half) {
