@@ -31,13 +31,14 @@
  *    p_a * theta^(-2j/d_a), p_a being the token's position on that axis:
  *      y[2j]   = x[2j] cos - x[2j+1] sin,   y[2j+1] = x[2j] sin + x[2j+1] cos.
  *    Each width must be even and >= 0, d_f + d_h + d_w == D, theta > 0.
- *  Rounding.  All arithmetic is fp32 (MFMA accumulates bf16 products in fp32);
- *    every fp32 -> bf16 rounding is round-to-nearest-even.  Rotated keys are
- *    rounded to bf16 before the score products; a rotated query is carried as
- *    hi + lo (hi = RNE_bf16(x); lo = x - hi, which the forward multiplies in
- *    fp8 e4m3 after a per-row power-of-two scaling against an fp8 copy of the
- *    rotated keys, and the backward in bf16), so scores lose precision mainly
- *    to the keys' bf16 rounding.
+ *  Rounding.  All arithmetic is fp32 (MFMA accumulates in fp32); every
+ *    fp32 -> bf16 or fp16 rounding is round-to-nearest-even.  With RoPE the
+ *    score product runs in fp16: each rotated query row and each 64-key tile
+ *    of rotated keys is scaled by a power of two that puts its largest
+ *    |element| in [2^14, 2^15) and rounded to fp16 (exact rescaling, any
+ *    finite input); the forward undoes the powers of two in fp32.  Without
+ *    RoPE the bf16 inputs enter the products unrounded.  P is rounded to bf16
+ *    for the PV product; the softmax sums use the unrounded fp32 values.
  *  Memory.  Every pointer is device memory owned by the caller, which keeps it
  *    alive until the stream's work has finished.  bf16 buffers, the rope table
  *    and workspaces must be 16-byte aligned; fp32 and int32 buffers 4-byte
@@ -122,12 +123,13 @@ int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D,
  * table == NULL: no rotation (g and r are then ignored).
  * lse may be NULL (not written).  scale: any finite value (1/sqrt(D) usual).
  * Workspace (required, 16-byte aligned): wanattn_self_fwd_workspace_bytes(B, L,
- * H, D, table != NULL) bytes.  It receives V transposed into 64-key tiles
- * (bf16 [B, H, ceil(L/64), D, 64], zero-padded: the PV product's operand
- * layout) and, with a table, the rotated keys as bf16 [B, L, H, D] and again
- * as fp8 e4m3 [B, L, H, D] (the fp8 copy serves the low-order part of the
- * rotated query's hi + lo split); each part starts on a 256-byte boundary.
- * Its contents on return are unspecified.
+ * H, D, table != NULL) bytes.  It receives K and V rewritten in 64-key tiles
+ * of every (b, h), zero-padded: K as [B, H, ceil(L/64), 64, D] (bf16, or with
+ * a table the rotated keys in fp16 with one power-of-two exponent per tile,
+ * the exponents following as int32 [B, H, ceil(L/64)]) and V transposed as
+ * [B, H, ceil(L/64), D, 64] bf16 (the PV product's operand layout); each
+ * part starts on a 256-byte boundary.  Its contents on return are
+ * unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 

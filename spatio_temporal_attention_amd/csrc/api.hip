@@ -85,14 +85,15 @@ WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, vo
   if (rc != WANATTN_OK) return rc;
   const hipStream_t s = (hipStream_t)stream;
   const RopeDev rope = make_rope(g, r, table);
-  // K (rotated once, instead of on every query tile's visit; also as fp8 for
-  // the low-order part of the split query) and V are rewritten in the
-  // forward's 64-key tile layout in one pass; queries are rotated on load.
+  // K (with RoPE rotated once, instead of on every query tile's visit, and
+  // stored in fp16 with a power-of-two exponent per tile) and V are rewritten
+  // in the forward's 64-key tile layout in one pass; queries are rotated on
+  // load.
   const FwdWsLayout wl = self_fwd_ws_layout(B, L, H, D, table != nullptr);
   uint16_t* kt = (uint16_t*)((uint8_t*)ws + wl.kt);
   uint16_t* vt = (uint16_t*)((uint8_t*)ws + wl.vt);
-  uint8_t* k8t = table != nullptr ? (uint8_t*)ws + wl.k8t : nullptr;
-  const int e = hip_status(launch_kv_tiles((const uint16_t*)k, (const uint16_t*)v, kt, k8t, vt, B, L, H, rope, s));
+  int* kexp = table != nullptr ? (int*)((uint8_t*)ws + wl.kexp) : nullptr;
+  const int e = hip_status(launch_kv_tiles((const uint16_t*)k, (const uint16_t*)v, kt, kexp, vt, B, L, H, rope, s));
   if (e != WANATTN_OK) return e;
   FwdParams p{};
   p.q = (const uint16_t*)q;
@@ -102,7 +103,7 @@ WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, vo
   p.lse = lse;
   p.k_lens = nullptr;
   p.kt = kt;
-  p.k8t = k8t;
+  p.kexp = kexp;
   p.vt = vt;
   p.rope = rope;
   p.B = B;

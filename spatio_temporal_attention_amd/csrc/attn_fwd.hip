@@ -12,13 +12,14 @@
 //  * each wave keeps its 32 rotated query rows in registers as the B operand
 //    of S^T = K Q^T (bf16 MFMA 32x32x16), so every lane owns one query row and
 //    the softmax needs one cross-lane step (lane l <-> l^32) per tile;
-//  * SPLIT_Q (with RoPE): the rotated query is carried as hi + lo, hi =
-//    RNE_bf16(q~) and lo = q~ - hi.  A single bf16 rounding of the rotated
-//    query moves LSE by up to ~1.2e-3 at 720p (tail of the row distribution).
-//    lo is ~2^-9 of q~, so its product needs few bits: it runs as a scaled
-//    fp8 MFMA (32x32x64, e4m3, twice the bf16 rate) of lo * 2^e (per-row
-//    power of two, undone by the E8M0 scale operand) against an fp8 copy of
-//    the rotated keys; the score error is then set by the keys' bf16 rounding;
+//  * F16 (with RoPE): the score product runs in fp16 (3 more mantissa bits
+//    than bf16, same MFMA rate).  The rotated query row is scaled by 2^-e_q
+//    so that its largest |element| lies in [2^14, 2^15) and rounded to fp16;
+//    the key pre-pass does the same per 64-key tile (exponent e_t); the
+//    softmax applies s = scale * 2^(e_q + e_t) * S.  Rounding the rotated
+//    query to bf16 instead would move LSE by up to ~1.2e-3 at 720p: a query's
+//    rounding error shifts all its scores coherently; in fp16 it is 8x
+//    smaller.  Without RoPE the inputs are used as given (bf16, exact);
 //  * K and V tiles of 64 keys go global -> LDS directly (global_load_lds,
 //    row-major, swizzled), double-buffered: the next tile's loads are in
 //    flight while the current one is multiplied;
@@ -46,10 +47,9 @@ constexpr int FWD_BR = 32 * FWD_WAVES;   // query rows per workgroup
 constexpr int FWD_BC = TILE_ROWS;         // keys per tile
 constexpr float RESCALE_SLACK = 8.0f;     // log2 units: P stays <= 256 between rescales
 
-template <bool POS_SCALE, bool SPLIT_Q, bool TILED>
+template <bool POS_SCALE, bool F16, bool TILED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE_ELEMS];   // [buffer][K|V]
-  __shared__ __attribute__((aligned(16))) uint8_t k8mem[SPLIT_Q ? 2 : 1][SPLIT_Q ? TILE_ELEMS : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,81 +77,48 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   // ---- query fragments (B operand of S^T = K Q^T): lane holds row i, d in [16s + 8*half, +8)
   const int i = qt * FWD_BR + wave * 32 + col;
   const bool row_ok = i < p.Lq;
-  bf16x8 qf[8];
-  i32x8 ql8[SPLIT_Q ? 2 : 1];   // low-order part of the rotated query, fp8, B layout of 32x32x64
-  int q_scale = 127;            // E8M0 scale undoing the per-row power of two applied to ql8
+  bf16x8 qf[8];       // F16: fp16 bit patterns
+  float g_q = p.scale_log2;   // score factor of this row: s * log2(e) = g_q * 2^e_t * S
   {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
-    // With SPLIT_Q the query carries the softmax scale: q' = c2 * R(p) q in
-    // fp32 (c2 = scale * log2 e), so S = K q' is already in the log2 domain.
-    auto rotate_pair = [&](uint32_t w, int pair, float& y0, float& y1) {
-      y0 = bf16_lo(w);
-      y1 = bf16_hi(w);
-      rope_rotate(y0, y1, rope_cs(p.rope, pos, pair), false);
-      y0 *= p.scale_log2;
-      y1 *= p.scale_log2;
-    };
+    if (F16) {
+      float y[8][8];   // rotated query, fp32
+      float mq = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      const int c = 2 * s + half;
-      if (row_ok) {
-        x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
-        if (SPLIT_Q) {
+      for (int s = 0; s < 8; ++s) {
+        const int c = 2 * s + half;
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (row_ok) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float y0, y1;
-            rotate_pair(x[t], 4 * c + t, y0, y1);
-            x[t] = pack_bf16(y0, y1);
-          }
-        } else if (p.rope.table != nullptr) {
-          x = rope_chunk(p.rope, pos, c, x, false);
+        for (int t = 0; t < 4; ++t) {
+          float y0 = bf16_lo(x[t]);
+          float y1 = bf16_hi(x[t]);
+          if (row_ok) rope_rotate(y0, y1, rope_cs(p.rope, pos, 4 * c + t), false);
+          y[s][2 * t] = y0;
+          y[s][2 * t + 1] = y1;
+          mq = fmaxf(mq, fmaxf(fabsf(y0), fabsf(y1)));
         }
       }
-      qf[s] = __builtin_bit_cast(bf16x8, x);
-    }
-    if (SPLIT_Q) {
-      // lo = q' - RNE_bf16(q') for head dims [64 ks + 32 half, +32), scaled
-      // by 2^e so the row's largest |lo| lands in [128, 256), as fp8.
-      float lo[2][32];
-      float mlo = 0.f;
+      const int e_q = pow2_exponent_15(xor32_max(mq));
+      g_q = ldexpf(p.scale_log2, e_q);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int s = 0; s < 8; ++s) {
+        u32x4 w;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int c = 8 * ks + 4 * half + cc;
-          u32x4 x = u32x4{0u, 0u, 0u, 0u};
-          if (row_ok) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float x0 = 0.f, x1 = 0.f;
-            if (row_ok) rotate_pair(x[t], 4 * c + t, x0, x1);
-            const uint32_t hb = pack_bf16(x0, x1);
-            const float l0 = x0 - bf16_lo(hb);
-            const float l1 = x1 - bf16_hi(hb);
-            lo[ks][8 * cc + 2 * t] = l0;
-            lo[ks][8 * cc + 2 * t + 1] = l1;
-            mlo = fmaxf(mlo, fmaxf(fabsf(l0), fabsf(l1)));
-          }
-        }
+        for (int t = 0; t < 4; ++t) w[t] = pack_f16(ldexpf(y[s][2 * t], -e_q), ldexpf(y[s][2 * t + 1], -e_q));
+        qf[s] = __builtin_bit_cast(bf16x8, w);
       }
-      mlo = xor32_max(mlo);
-      int e = 0;
-      if (mlo > 0.f) {
-        int ex;
-        frexpf(mlo, &ex);         // mlo = f * 2^ex, f in [0.5, 1)
-        e = min(max(8 - ex, -100), 100);
-      }
-      q_scale = 127 - e;
-      const float sc = ldexpf(1.f, e);
+    } else {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          ql8[ks][w] = (int)pack_fp8x4(lo[ks][4 * w] * sc, lo[ks][4 * w + 1] * sc, lo[ks][4 * w + 2] * sc,
-                                       lo[ks][4 * w + 3] * sc);
+      for (int s = 0; s < 8; ++s) {
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        const int c = 2 * s + half;
+        if (row_ok) {
+          x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
+          if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
         }
+        qf[s] = __builtin_bit_cast(bf16x8, x);
       }
     }
   }
@@ -161,47 +128,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   for (int d = 0; d < 4; ++d) o_acc[d] = f32x16{};
   float m_run = -INFINITY;   // running max of scale*log2e*s (this lane's row)
   float l_run = 0.f;         // this lane's partial exp-sum (the other half holds the rest)
-  const float c2 = p.scale_log2;
-  // SPLIT_Q: the score MFMAs start from -m_c (m_c = m_run once finite, 0
-  // before), so the accumulator holds S - m_c and P = exp2 of it directly.
-  float m_c = 0.f;
-  f32x16 neg_m = f32x16{};
+  const int* kexp = F16 ? p.kexp + tile0 : nullptr;   // e_t of each key tile
 
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 
   // One 64-key tile: scores, online softmax, O += P V.  MASK: the last tile,
   // whose keys past n_keys get -inf (full tiles carry no masking code).
-  auto tile_step = [&](auto mask_tag, const uint16_t* ks, const uint16_t* vs, const uint8_t* k8s, int t) {
+  auto tile_step = [&](auto mask_tag, const uint16_t* ks, const uint16_t* vs, int t, int e_t) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // log2-domain factor of this tile's raw scores
+    const float g = F16 ? ldexpf(g_q, e_t) : g_q;
     // S^T (64 keys x 32 queries) as two 32x32 blocks.
     f32x16 s_acc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s_acc[kb] = SPLIT_Q ? neg_m : f32x16{};
+      s_acc[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
-        s_acc[kb] = mfma32(a, qf[s], s_acc[kb]);
-      }
-      if (SPLIT_Q) {
-        // + fp8 keys x fp8 low-order query, the row's 2^e undone by the MFMA scale
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const i32x8 a8 = lds_row_frag8(k8s, kb * 32 + col, k2, half);
-          s_acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, ql8[k2], s_acc[kb], 0, 0, 0, 127, 0,
-                                                                     q_scale);
-        }
+        s_acc[kb] = F16 ? mfma32_f16(a, qf[s], s_acc[kb]) : mfma32(a, qf[s], s_acc[kb]);
       }
     }
 
-    // Scores: SPLIT_Q S - m_c (log2 domain); else raw for a positive scale,
-    // otherwise already scaled to the log2 domain.
+    // Scores: raw for a positive scale, otherwise already scaled to the log2 domain.
     float sv[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x = (SPLIT_Q || POS_SCALE) ? s_acc[kb][j] : s_acc[kb][j] * c2;
+        float x = POS_SCALE ? s_acc[kb][j] : s_acc[kb][j] * g;
         if (MASK) {
           const int key = t * FWD_BC + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
           if (key >= n_keys) x = -INFINITY;
@@ -215,8 +170,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
     mx = xor32_max(mx);
-    if (SPLIT_Q) mx += m_c;
-    else if (POS_SCALE) mx *= c2;   // max(s) * c == max(s * c) for c > 0
+    if (POS_SCALE) mx *= g;   // max(s) * g == max(s * g) for g > 0
 
     // Lazy rescaling: the running max only moves when some row's tile max
     // exceeds it by more than RESCALE_SLACK (log2 units), so p <= 2^SLACK and
@@ -229,16 +183,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
-      if (SPLIT_Q) {
-        const float delta = m_new - m_c;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sv[kb][j] -= delta;
-        m_c = m_new;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) neg_m[j] = -m_new;
-      }
     }
 
     // P in bf16 (RNE) for PV; l sums P in fp32 (summing the rounded values
@@ -250,8 +194,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       float pv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (SPLIT_Q) pv[j] = __builtin_amdgcn_exp2f(sv[kb][j]);
-        else if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
+        if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], g, -m_run));
         else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
         psum += pv[j];
       }
@@ -273,19 +216,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   if (n_tiles > 0) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t koff[4], voff[4], k8off[2];
+    uint32_t koff[4], voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       koff[i] = ktile_lane_off(wv, i, lane);
       voff[i] = rows128_lane_off<4>(wv, i, lane);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) k8off[i] = rows128_lane_off<2>(wv, i, lane);
     const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(TILED ? p.kt + tile0 * TILE_ELEMS : p.k, bytes);
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(TILED ? p.vt + tile0 * TILE_ELEMS : p.v, bytes);
-    const __amdgpu_buffer_rsrc_t k8rs = tile_rsrc(SPLIT_Q ? p.k8t + tile0 * TILE_ELEMS : nullptr, bytes / 2);
-    // Stage tile t of K (bf16, and fp8 with SPLIT_Q) and V into buffer `buf`.
+    // Stage tile t of K and V into buffer `buf`.
     auto stage = [&](int buf, int t) {
       if (TILED) {
         const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
@@ -296,16 +236,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
           buf_dma16(krs, koff[i], soff, kl + 1024 * i);
           buf_dma16(vrs, voff[i], soff, vl + 1024 * i);
         }
-        if (SPLIT_Q) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) buf_dma16(k8rs, k8off[i], soff / 2, k8mem[buf] + 2048 * wv + 1024 * i);
-        }
       } else {
         tile_dma(smem[buf][0], kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
         tile_dma(smem[buf][1], vbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
       }
     };
+    // A tile's exponent is loaded with its copies, so the wait that ends the
+    // previous tile covers it.
     stage(0, 0);
+    int e_cur = F16 ? kexp[0] : 0;
     wait_vmem();
     __syncthreads();
     // Full tiles in the loop; a partial last tile is peeled off after it.
@@ -313,13 +252,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     for (int t = 0; t < n_full; ++t) {
       const int buf = t & 1;
       const bool has_next = t + 1 < n_tiles;
-      if (has_next) stage(buf ^ 1, t + 1);
-      tile_step(std::false_type{}, smem[buf][0], smem[buf][1], k8mem[SPLIT_Q ? buf : 0], t);
+      int e_next = 0;
+      if (has_next) {
+        stage(buf ^ 1, t + 1);
+        if (F16) e_next = kexp[t + 1];
+      }
+      tile_step(std::false_type{}, smem[buf][0], smem[buf][1], t, e_cur);
       if (has_next) wait_vmem();
       __syncthreads();
+      e_cur = e_next;
     }
     if (n_full < n_tiles)
-      tile_step(std::true_type{}, smem[n_full & 1][0], smem[n_full & 1][1], k8mem[SPLIT_Q ? (n_full & 1) : 0], n_full);
+      tile_step(std::true_type{}, smem[n_full & 1][0], smem[n_full & 1][1], n_full, e_cur);
   }
 
   // ---- epilogue: O = O / l (bf16), LSE = ln sum exp(s) = ln2 * (m + log2 l)
@@ -353,23 +297,22 @@ hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)q.n_qtiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)total), block(256);
-  // With RoPE the rotated query is carried as bf16 hi + fp8 lo (see SPLIT_Q),
-  // which needs the tiled fp8 copy of the rotated keys (self-attention only).
-  const bool split = p.rope.table != nullptr;
+  // With RoPE the scores run in fp16 (see F16) against the fp16 key tiles
+  // and their exponents (self-attention only).
+  const bool f16 = p.rope.table != nullptr;
   const bool vt = p.kt != nullptr;
   if (vt && (p.vt == nullptr || p.k_lens != nullptr || p.Lk != p.Lq)) return hipErrorInvalidValue;
   // The tiles of one (b, h) are addressed through a buffer resource of 32-bit extent.
   if (vt && (int64_t)((p.Lk + FWD_BC - 1) / FWD_BC) * (TILE_ELEMS * 2) > (int64_t)0xffffffff)
     return hipErrorInvalidValue;
-  if (split && (p.k8t == nullptr || !vt)) return hipErrorInvalidValue;
-  if (split) {
-    // The scale rides on the query (any sign).
-    hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, q);
-  } else if (p.scale_log2 > 0.f) {
-    if (vt) hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, q);
+  if (f16 && (p.kexp == nullptr || !vt)) return hipErrorInvalidValue;
+  if (p.scale_log2 > 0.f) {
+    if (f16) hipLaunchKernelGGL((attn_fwd_kernel<true, true, true>), grid, block, 0, stream, q);
+    else if (vt) hipLaunchKernelGGL((attn_fwd_kernel<true, false, true>), grid, block, 0, stream, q);
     else hipLaunchKernelGGL((attn_fwd_kernel<true, false, false>), grid, block, 0, stream, q);
   } else {
-    if (vt) hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, q);
+    if (f16) hipLaunchKernelGGL((attn_fwd_kernel<false, true, true>), grid, block, 0, stream, q);
+    else if (vt) hipLaunchKernelGGL((attn_fwd_kernel<false, false, true>), grid, block, 0, stream, q);
     else hipLaunchKernelGGL((attn_fwd_kernel<false, false, false>), grid, block, 0, stream, q);
   }
   return hipGetLastError();

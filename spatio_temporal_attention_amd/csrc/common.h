@@ -26,7 +26,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ---------------------------------------------------------------------------
@@ -42,16 +43,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// Four fp32 -> packed OCP fp8 e4m3 (round to nearest even), saturated to +-448
-// so that out-of-range values never become NaN.
-__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  constexpr float M = 448.f;
-  a = fminf(fmaxf(a, -M), M);
-  b = fminf(fmaxf(b, -M), M);
-  c = fminf(fmaxf(c, -M), M);
-  d = fminf(fmaxf(d, -M), M);
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+// Two fp32 -> packed fp16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f32x2 v = {a, b};
+  f16x2 h = __builtin_convertvector(v, f16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// The e for which x * 2^-e lies in [2^14, 2^15) (0 for x == 0): scaling a
+// row or tile by 2^-e puts its largest magnitude at the top of the fp16
+// range, below its maximum 65504, with full fp16 precision below it.
+__device__ __forceinline__ int pow2_exponent_15(float x) {
+  if (!(x > 0.f)) return 0;
+  int ex;
+  frexpf(x, &ex);   // x = f * 2^ex, f in [0.5, 1)
+  return ex - 15;
 }
 
 // ---------------------------------------------------------------------------
@@ -226,13 +232,6 @@ __device__ __forceinline__ bf16x8 lds_vt_frag(const uint16_t* lds, int row, int 
 }
 
 
-// fp8 MFMA 32x32x64 A-side fragment: lane l gets bytes [64*ks + 32*(l/32), +32) of `row`.
-__device__ __forceinline__ i32x8 lds_row_frag8(const uint8_t* lds, int row, int ks, int half) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + tile8_off(row, 4 * ks + 2 * half));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + tile8_off(row, 4 * ks + 2 * half + 1));
-  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
 // 16-byte row fragment: elements [8*chunk, 8*chunk+8) of `row`.
 __device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t* lds, int row, int chunk) {
   return *reinterpret_cast<const bf16x8*>(lds + tile_off(row, chunk * 8));
@@ -268,6 +267,11 @@ __device__ __forceinline__ bf16x8 lds_col_frag(const uint16_t* lds, int rbase, i
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The same product with both operands holding fp16 bit patterns.
+__device__ __forceinline__ f32x16 mfma32_f16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
 }
 
 // Pack accumulator entries 8g .. 8g+7 (after an elementwise map already

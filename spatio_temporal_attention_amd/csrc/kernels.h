@@ -18,8 +18,8 @@ struct FwdParams {
   const int32_t* k_lens;    // [B] valid key counts or nullptr (all Lk)
   // Self-attention: k and v in the tile layout of launch_kv_tiles (then k/v
   // above are unused), [B, H, ceil(Lk/64)] tiles; nullptr: read k/v directly.
-  const uint16_t* kt;       // keys (rotated with RoPE), tiles of [64][128] bf16
-  const uint8_t* k8t;       // the same keys as fp8 e4m3, tiles of [64][128] (with RoPE), or nullptr
+  const uint16_t* kt;       // keys, tiles of [64][128]: bf16, or with RoPE fp16 of R(p) k * 2^-e_t
+  const int* kexp;          // with RoPE: e_t of every tile, else nullptr
   const uint16_t* vt;       // V^T, tiles of [128][64] bf16
   RopeDev rope;             // rope.table == nullptr: queries are not rotated
   int B, Lq, Lk, H;
@@ -53,8 +53,8 @@ hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int B, int L, int H, co
                          bool inverse, hipStream_t stream);
 hipError_t launch_rope3d_split(const uint16_t* x, uint16_t* hi, uint16_t* lo, int B, int L, int H,
                                const RopeDev& rope, hipStream_t stream);
-hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, uint8_t* k8t, uint16_t* vt, int B,
-                           int L, int H, const RopeDev& rope, hipStream_t stream);
+hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, int* kexp, uint16_t* vt, int B, int L,
+                           int H, const RopeDev& rope, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_delta(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);

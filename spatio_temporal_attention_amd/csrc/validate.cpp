@@ -46,13 +46,14 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
   FwdWsLayout w{0, 0, 0, 0};
   if (check_dims(B, L, H, D) != WANATTN_OK) return w;
-  const size_t tile_elems = (size_t)B * H * (((size_t)L + 63) / 64) * 64 * (size_t)D;
-  w.kt = 0;                                   // K~ tiles [B, H, tile, 64, D] bf16
+  const size_t tiles = (size_t)B * H * (((size_t)L + 63) / 64);
+  const size_t tile_elems = tiles * 64 * (size_t)D;
+  w.kt = 0;                                   // K tiles [B, H, tile, 64, D], bf16 or fp16
   w.vt = align256(tile_elems * 2);            // V^T tiles [B, H, tile, D, 64] bf16
   w.total = align256(w.vt + tile_elems * 2);
   if (with_rope) {
-    w.k8t = w.total;                          // K~ tiles [B, H, tile, 64, D] fp8 e4m3
-    w.total = w.k8t + tile_elems;
+    w.kexp = w.total;                         // exponent of every K tile, int32 [B, H, tile]
+    w.total = w.kexp + tiles * 4;
   }
   return w;
 }

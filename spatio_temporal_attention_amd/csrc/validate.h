@@ -20,11 +20,12 @@ int check_scale(float scale);
 bool aligned(const void* p, size_t a);
 int64_t rope_table_entries(wanattn_grid g, wanattn_rope r);   // (cos, sin) pairs; -1 if invalid
 
-// Forward workspace, in 64-key tiles of every (b, h): K (rotated with RoPE)
-// as bf16, V^T as bf16, then with RoPE the rotated keys as fp8; each part
-// starts on a 256-byte boundary.
+// Forward workspace, in 64-key tiles of every (b, h): K (bf16, or with RoPE
+// the rotated keys in fp16 with a power-of-two exponent per tile), V^T
+// (bf16), then with RoPE the tile exponents (int32); each part starts on a
+// 256-byte boundary.
 struct FwdWsLayout {
-  size_t kt, vt, k8t, total;   // byte offsets of the parts and the total size
+  size_t kt, vt, kexp, total;   // byte offsets of the parts and the total size
 };
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope);
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);

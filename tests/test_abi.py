@@ -64,8 +64,9 @@ def test_workspace_sizes(lib):
     n = B * L * H * D
     tiled = B * H * ((L + 63) // 64) * 64 * D           # elements of K or V in 64-key tiles, zero-padded
     assert tiled > n
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 2 * tiled * 2          # K~ and V^T, bf16
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + tiled  # + K~ in fp8
+    n_tiles = B * H * ((L + 63) // 64)
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 2 * tiled * 2          # K and V^T tiles
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + 4 * n_tiles  # + tile exponents
     assert lib.wanattn_self_fwd_workspace_bytes(1, 1, 1, D, 0) == 2 * 64 * D * 2
     delta = (B * H * L * 4 + 255) // 256 * 256
     assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta
