@@ -210,8 +210,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16/fp16",
         "data": "synthetic (seeded N(0,1) bf16; no dataset or weights involved)",
+        "compute": "bf16 in/out; with RoPE the QK^T MFMAs take fp16 (rotated q/k rescaled by powers of two), "
+                   "PV and the backward's gradient products bf16; fp32 accumulation and softmax",
         "config": {"workload": "wan14b-720p self-attn fwd+bwd + text cross-attn",
                    "grid": list(w.grid), "B": B, "L": L, "H": H, "D": D, "rope_split": [48, 40, 40],
                    "rope_theta": 10000.0, "text_tokens": 512, "parallelism": "none (1 GPU)",
@@ -220,7 +222,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
-                     "kernel": "attn_fwd_kernel (+ key pre-rotation inside the same timed call)",
+                     "kernel": "attn_fwd_kernel (+ the K/V tile prep pass inside the same timed call)",
                      "flop_per_launch": fwd_flop},
     }
     result.update(extra)
