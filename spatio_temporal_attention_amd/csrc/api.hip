@@ -125,40 +125,40 @@ WANATTN_API int wanattn_self_bwd(const void* q, const void* k, const void* v, co
   const int rc = validate_self_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, L, H, D, g, r, table, scale, ws, ws_bytes);
   if (rc != WANATTN_OK) return rc;
   const hipStream_t s = (hipStream_t)stream;
+  // Prep passes: Q and K (rotated with a table) as fp16 tiles with the
+  // forward's power-of-two exponents, their bf16 transposes, dO and V tiles,
+  // and Delta; then the dK/dV and dQ passes over those tiles.
+  const BwdWsLayout w = self_bwd_ws_layout(B, L, H, D);
+  uint8_t* base = (uint8_t*)ws;
   BwdParams p{};
-  const size_t delta_bytes = ((size_t)B * H * L * 4 + 255) & ~(size_t)255;
-  p.delta = (float*)ws;
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k;
-  p.rope = make_rope(g, r, table);
-  p.q_lo = nullptr;
-  if (table != nullptr) {
-    // Rotated queries as bf16 hi + lo (exactly as the forward rotated them),
-    // rotated keys as bf16: the recomputed scores match the forward's.
-    uint16_t* qh = (uint16_t*)((char*)ws + delta_bytes);
-    uint16_t* ql = qh + (size_t)B * L * H * D;
-    uint16_t* kr = ql + (size_t)B * L * H * D;
-    int e = hip_status(launch_rope3d_split((const uint16_t*)q, qh, ql, B, L, H, p.rope, s));
-    if (e != WANATTN_OK) return e;
-    e = hip_status(launch_rope3d((const uint16_t*)k, kr, B, L, H, p.rope, false, s));
-    if (e != WANATTN_OK) return e;
-    p.q = qh;
-    p.q_lo = ql;
-    p.k = kr;
-  }
-  p.v = (const uint16_t*)v;
-  p.o = (const uint16_t*)o;
-  p.dout = (const uint16_t*)dout;
+  p.qf = (const uint16_t*)(base + w.qf);
+  p.qexp = (const int*)(base + w.qexp);
+  p.qt = (const uint16_t*)(base + w.qt);
+  p.dor = (const uint16_t*)(base + w.dor);
+  p.dot = (const uint16_t*)(base + w.dot);
+  p.kf = (const uint16_t*)(base + w.kf);
+  p.kexp = (const int*)(base + w.kexp);
+  p.kt = (const uint16_t*)(base + w.kt);
+  p.vr = (const uint16_t*)(base + w.vr);
   p.lse = lse;
+  p.delta = (const float*)(base + w.delta);
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
+  p.rope = make_rope(g, r, table);
   p.B = B;
   p.L = L;
   p.H = H;
   p.scale = scale;
   p.scale_log2 = scale * LOG2E_F;
-  int e = hip_status(launch_bwd_delta(p, s));
+  int e = hip_status(launch_bwd_k_tiles((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)(base + w.kf),
+                                        (int*)(base + w.kexp), (uint16_t*)(base + w.kt), (uint16_t*)(base + w.vr), B,
+                                        L, H, p.rope, s));
+  if (e != WANATTN_OK) return e;
+  e = hip_status(launch_bwd_q_tiles((const uint16_t*)q, (const uint16_t*)dout, (const uint16_t*)o,
+                                    (uint16_t*)(base + w.qf), (int*)(base + w.qexp), (uint16_t*)(base + w.qt),
+                                    (uint16_t*)(base + w.dor), (uint16_t*)(base + w.dot), (float*)(base + w.delta), B,
+                                    L, H, p.rope, s));
   if (e != WANATTN_OK) return e;
   e = hip_status(launch_bwd_dkdv(p, s));
   if (e != WANATTN_OK) return e;

@@ -1,27 +1,31 @@
-// Self-attention backward for gfx950, as two deterministic passes plus a
-// row-statistics pre-pass.  The formulas are the calculus of the forward
-// (full spatio-temporal attention with 3D RoPE; "Wan Team, Alibaba (2025)",
-// Key takeaways, Backbone; training in bf16 per the Wan2.1 reading notes,
-// 3. Training):
-//   Delta_i = <dO_i, O_i>
-//   P_ij    = exp(scale <q~_i, k~_j> - LSE_i)           (recomputed, never stored)
+// Self-attention backward for gfx950: two deterministic passes over the
+// tiles the prep passes write (kv_prep.hip).  The formulas are the calculus
+// of the forward (full spatio-temporal attention with 3D RoPE; "Wan Team,
+// Alibaba (2025)", Key takeaways, Backbone; training in bf16 per the Wan2.1
+// reading notes, 3. Training):
+//   Delta_i = <dO_i, O_i>                                  (prep pass)
+//   P_ij    = exp(scale <q~_i, k~_j> - LSE_i)              (recomputed, never stored)
 //   dV_j    = sum_i P_ij dO_i
 //   dS_ij   = P_ij (<dO_i, v_j> - Delta_i)
 //   dq~_i   = scale sum_j dS_ij k~_j,   dk~_j = scale sum_i dS_ij q~_i
 //   dq_i    = R(p_i)^T dq~_i,           dk_j  = R(p_j)^T dk~_j
-// q~ and k~ arrive pre-rotated (q~ as a bf16 hi + lo pair, exactly as the
-// forward used it, so the recomputed P matches the forward's LSE); the inverse
-// rotation is fused into the dQ and dK stores.  Tiles move global -> LDS by
-// direct loads (global_load_lds), double-buffered.
+// The scores are recomputed from the same fp16 operands the forward used
+// (q~ and k~ per 64-token tile scaled by 2^-e and rounded to fp16), so P
+// matches the forward's LSE; s * log2(e) = scale*log2(e) * 2^(e_q + e_k) * S.
+// The gradient products take bf16 operands (P, dS, dO, V, q~^T, k~^T).
+// Every MFMA operand comes from a plain 16-byte LDS read or from registers:
+// operands contracted over tokens come from T tiles (token-position order
+// matching the accumulator registers), so no LDS transpose read is needed.
+// The inverse rotation is fused into the dQ and dK stores.
 //
-//  * bwd_delta: Delta per row (memory-bound).
-//  * bwd_dkdv:  workgroup = 128 keys (4 waves x 32), loop over 64-query tiles.
-//               S = Q~ K~^T and dP = dO V^T with the wave's K~/V rows held in
-//               registers as MFMA B operands (lane owns key column j);
-//               dV^T += dO^T P and dK~^T += Q~^T dS read Q~/dO through the LDS
-//               transpose read and take P/dS from the accumulators.
-//  * bwd_dq:    workgroup = 128 queries, loop over 64-key tiles; S^T = K~ Q~^T,
-//               dP^T = V dO^T (lane owns query row i), dQ~^T += K~^T dS^T.
+//  * bwd_dkdv: workgroup = 128 keys (4 waves x 32, one wave per SIMD and up
+//    to 512 registers: K and V rows of the wave's keys stay in registers),
+//    loop over 64-query tiles staged as Q fp16 rows, (R q)^T, dO rows, dO^T.
+//    S = Q K^T and dP = dO V^T (lane owns key j); dV^T += dO^T P and
+//    dK~^T += (R q)^T dS take P / dS from the accumulators.
+//  * bwd_dq:   workgroup = 256 queries (8 waves, two per SIMD), loop over
+//    64-key tiles staged as K fp16 rows, (R k)^T, V rows.  S^T = K Q^T,
+//    dP^T = V dO^T (lane owns query i), dQ~^T += (R k)^T dS^T.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,35 +34,8 @@ namespace wanattn {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
-
-// Delta_i = <dO_i, O_i>; 16 lanes per row (one 16-byte chunk each).
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  const int64_t rows = (int64_t)p.B * p.L * p.H;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t tix = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; tix < rows * 16; tix += stride) {
-    const int64_t row = tix >> 4;
-    const int c = (int)(tix & 15);
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + row * HD + c * 8);
-    const u32x4 o = *reinterpret_cast<const u32x4*>(p.o + row * HD + c * 8);
-    float s = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      s = fmaf(bf16_lo(a[t]), bf16_lo(o[t]), s);
-      s = fmaf(bf16_hi(a[t]), bf16_hi(o[t]), s);
-    }
-    s += __shfl_xor(s, 8, 16);
-    s += __shfl_xor(s, 4, 16);
-    s += __shfl_xor(s, 2, 16);
-    s += __shfl_xor(s, 1, 16);
-    if (c == 0) {
-      const int h = (int)(row % p.H);
-      const int64_t bn = row / p.H;
-      const int n = (int)(bn % p.L);
-      const int b = (int)(bn / p.L);
-      p.delta[((int64_t)b * p.H + h) * p.L + n] = s;
-    }
-  }
-}
+constexpr int DKDV_WAVES = 4;
+constexpr int DQ_WAVES = 8;
 
 // Store 4 consecutive head-dim elements [d0, d0+4) of token n (two rotary
 // pairs), optionally rotated back by minus the angle, as bf16.
@@ -74,14 +51,22 @@ __device__ __forceinline__ void store_grad4(uint16_t* row_ptr, const RopeDev& ro
   *reinterpret_cast<u32x2*>(row_ptr + d0) = w;
 }
 
+// Row `r` of a row tile in global memory as the 8 register fragments of the
+// 32x32x16 operand layout (lane half `half` holds chunks 2s + half).
+__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* tile, int r, int half, bool ok) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (ok) x = *reinterpret_cast<const u32x4*>(tile + r * HD + (2 * s + half) * 8);
+    f[s] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup owns 128 keys; loop over query tiles of 64.
-// SPLIT: rotated queries come as bf16 hi + lo; S takes both (as the forward did).
+// dK, dV: workgroup owns 128 keys (key tiles 2kb, 2kb+1); loop over 64-query tiles.
 // ---------------------------------------------------------------------------
-template <bool SPLIT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NT = SPLIT ? 3 : 2;                                           // Q~ hi, [Q~ lo], dO
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][NT][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE_ELEMS];   // [buf][Q fp16 | (Rq)^T | dO | dO^T]
   __shared__ float lse2_s[2][TILE_ROWS];                                      // LSE * log2 e (+inf: no row)
   __shared__ float delta_s[2][TILE_ROWS];
 
@@ -93,33 +78,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = logical % p.n_tiles;
+  const int kb = logical % p.n_tiles;
   const int bh = logical / p.n_tiles;
   const int h = bh % p.H;
   const int b = bh / p.H;
+  const int nt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
+  const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
 
-  const int64_t rs = (int64_t)p.H * HD;
-  const int64_t head_off = ((int64_t)b * p.L * p.H + h) * HD;
-  const uint16_t* qbase = p.q + head_off;
-  const uint16_t* qlbase = SPLIT ? p.q_lo + head_off : nullptr;
-  const uint16_t* dobase = p.dout + head_off;
-  const float* lse_row = p.lse + ((int64_t)b * p.H + h) * p.L;
-  const float* delta_row = p.delta + ((int64_t)b * p.H + h) * p.L;
-
-  // This lane's key row j as B-operand fragments of K~ and V.
-  const int j = kt * 128 + wave * 32 + col;
+  // This lane's key j: row 32*(wave%2) + col of key tile 2kb + wave/2.
+  const int ktile = 2 * kb + (wv >> 1);
+  const int j = kb * 128 + wave * 32 + col;
   const bool key_ok = j < p.L;
-  bf16x8 kf[8], vf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4 xk = u32x4{0u, 0u, 0u, 0u}, xv = u32x4{0u, 0u, 0u, 0u};
-    if (key_ok) {
-      xk = *reinterpret_cast<const u32x4*>(p.k + head_off + (int64_t)j * rs + (2 * s + half) * 8);
-      xv = *reinterpret_cast<const u32x4*>(p.v + head_off + (int64_t)j * rs + (2 * s + half) * 8);
-    }
-    kf[s] = __builtin_bit_cast(bf16x8, xk);
-    vf[s] = __builtin_bit_cast(bf16x8, xv);
-  }
+  const bool tile_ok = ktile < nt;
+  bf16x8 kf[8], vf[8];   // K fp16 (bit patterns), V bf16: B operands of S and dP
+  load_row_frags(kf, p.kf + (tile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
+  load_row_frags(vf, p.vr + (tile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
+  const int e_k = tile_ok ? p.kexp[tile0 + ktile] : 0;
 
   f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
@@ -127,33 +101,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     dk_acc[d] = f32x16{};
     dv_acc[d] = f32x16{};
   }
-  const float c2 = p.scale_log2;
-  const int n_qt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
+  const float* lse_row = p.lse + ((int64_t)b * p.H + h) * p.L;
+  const float* delta_row = p.delta + ((int64_t)b * p.H + h) * p.L;
 
-  auto stage = [&](int buf, int row0) {
-    tile_dma(tiles[buf][0], qbase, rs, row0, p.L, wv, lane);
-    if (SPLIT) tile_dma(tiles[buf][1], qlbase, rs, row0, p.L, wv, lane);
-    tile_dma(tiles[buf][NT - 1], dobase, rs, row0, p.L, wv, lane);
+  uint32_t roff[4], toff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    roff[i] = rowtile_lane_off<DKDV_WAVES>(wv, i, lane);
+    toff[i] = ttile_lane_off<DKDV_WAVES>(wv, i, lane);
+  }
+  const uint32_t bytes = (uint32_t)nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+  const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t qtr = tile_rsrc(p.qt + tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t dor = tile_rsrc(p.dor + tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + tile0 * TILE_ELEMS, bytes);
+  const int* qexp = p.qexp + tile0;
+
+  auto stage = [&](int buf, int t) {
+    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      buf_dma16(qfr, roff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][0], wv, i));
+      buf_dma16(qtr, toff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][1], wv, i));
+      buf_dma16(dor, roff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][2], wv, i));
+      buf_dma16(dotr, toff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][3], wv, i));
+    }
     if (tid < TILE_ROWS) {
-      const int i = row0 + tid;
+      const int i = t * TILE_ROWS + tid;
       lse2_s[buf][tid] = (i < p.L) ? lse_row[i] * LOG2E : INFINITY;
     } else if (tid < 2 * TILE_ROWS) {
-      const int i = row0 + tid - TILE_ROWS;
+      const int i = t * TILE_ROWS + tid - TILE_ROWS;
       delta_s[buf][tid - TILE_ROWS] = (i < p.L) ? delta_row[i] : 0.f;
     }
   };
 
+  // A tile's exponent is loaded with its copies, so the wait that ends the
+  // previous tile covers it.
   stage(0, 0);
+  int e_q = qexp[0];
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < n_qt; ++t) {
+  for (int t = 0; t < nt; ++t) {
     const int buf = t & 1;
-    const bool has_next = t + 1 < n_qt;
-    if (has_next) stage(buf ^ 1, (t + 1) * TILE_ROWS);
+    const bool has_next = t + 1 < nt;
+    int e_q_next = 0;
+    if (has_next) {
+      stage(buf ^ 1, t + 1);
+      e_q_next = qexp[t + 1];
+    }
     const uint16_t* qs = tiles[buf][0];
-    const uint16_t* qls = tiles[buf][SPLIT ? 1 : 0];
-    const uint16_t* ds_ = tiles[buf][NT - 1];
+    const uint16_t* qts = tiles[buf][1];
+    const uint16_t* dos = tiles[buf][2];
+    const uint16_t* dots = tiles[buf][3];
+    const float g = ldexpf(p.scale_log2, e_q + e_k);
 
     bf16x8 pf[4], dsf[4];
 #pragma unroll
@@ -161,15 +162,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        s_acc = mfma32(lds_row_frag(qs, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-        if (SPLIT) s_acc = mfma32(lds_row_frag(qls, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-        dp_acc = mfma32(lds_row_frag(ds_, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
+        s_acc = mfma32_f16(lds_row_frag(qs, qb * 32 + col, 2 * s + half), kf[s], s_acc);
+        dp_acc = mfma32(lds_row_frag(dos, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
       }
       float pv[16], dsv[16];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int r = qb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);   // query row in the tile
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], c2, -lse2_s[buf][r]));
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2_s[buf][r]));
         pv[jj] = pe;
         dsv[jj] = pe * (dp_acc[jj] - delta_s[buf][r]);
       }
@@ -182,18 +182,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
       for (int qg = 0; qg < 4; ++qg) {
-        dv_acc[d] = mfma32(lds_col_frag(ds_, qg * 16, d * 32, lane), pf[qg], dv_acc[d]);
-        dk_acc[d] = mfma32(lds_col_frag(qs, qg * 16, d * 32, lane), dsf[qg], dk_acc[d]);
+        dv_acc[d] = mfma32(lds_vt_frag(dots, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
+        dk_acc[d] = mfma32(lds_vt_frag(qts, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
       }
     }
 
     if (has_next) wait_vmem();
     __syncthreads();
+    e_q = e_q_next;
   }
 
   if (key_ok) {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr) pos = token_pos(p.rope, j);
+    const int64_t rs = (int64_t)p.H * HD;
+    const int64_t head_off = ((int64_t)b * p.L * p.H + h) * HD;
     uint16_t* dkrow = p.dk + head_off + (int64_t)j * rs;
     uint16_t* dvrow = p.dv + head_off + (int64_t)j * rs;
     RopeDev none = p.rope;
@@ -213,11 +216,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup owns 128 queries; loop over key tiles of 64.
+// dQ: workgroup owns 256 queries (query tiles 4qb .. 4qb+3); loop over 64-key tiles.
 // ---------------------------------------------------------------------------
-template <bool SPLIT>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE_ELEMS];   // [buffer][K~ | V]
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][3][TILE_ELEMS];   // [buf][K fp16 | (Rk)^T | V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -227,59 +229,71 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = logical % p.n_tiles;
+  const int qb = logical % p.n_tiles;
   const int bh = logical / p.n_tiles;
   const int h = bh % p.H;
   const int b = bh / p.H;
+  const int nt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
+  const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
 
-  const int64_t rs = (int64_t)p.H * HD;
-  const int64_t head_off = ((int64_t)b * p.L * p.H + h) * HD;
-  const uint16_t* kbase = p.k + head_off;
-  const uint16_t* vbase = p.v + head_off;
-
-  const int i = qt * 128 + wave * 32 + col;
+  // This lane's query i: row 32*(wave%2) + col of query tile 4qb + wave/2.
+  const int qtile = 4 * qb + (wv >> 1);
+  const int i = qb * 256 + wave * 32 + col;
   const bool row_ok = i < p.L;
-  bf16x8 qf[8], dof[8];
-  bf16x8 ql[SPLIT ? 8 : 1];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4 xq = u32x4{0u, 0u, 0u, 0u}, xd = u32x4{0u, 0u, 0u, 0u}, xl = u32x4{0u, 0u, 0u, 0u};
-    if (row_ok) {
-      const int64_t off = head_off + (int64_t)i * rs + (2 * s + half) * 8;
-      xq = *reinterpret_cast<const u32x4*>(p.q + off);
-      xd = *reinterpret_cast<const u32x4*>(p.dout + off);
-      if (SPLIT) xl = *reinterpret_cast<const u32x4*>(p.q_lo + off);
-    }
-    qf[s] = __builtin_bit_cast(bf16x8, xq);
-    dof[s] = __builtin_bit_cast(bf16x8, xd);
-    if (SPLIT) ql[s] = __builtin_bit_cast(bf16x8, xl);
-  }
+  const bool tile_ok = qtile < nt;
+  bf16x8 qf[8], dof[8];   // Q fp16 (bit patterns), dO bf16: B operands of S^T and dP^T
+  load_row_frags(qf, p.qf + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
+  load_row_frags(dof, p.dor + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
+  const int e_q = tile_ok ? p.qexp[tile0 + qtile] : 0;
   const int64_t stat = ((int64_t)b * p.H + h) * p.L + i;
   const float lse2 = row_ok ? p.lse[stat] * LOG2E : INFINITY;
   const float delta = row_ok ? p.delta[stat] : 0.f;
-  const float c2 = p.scale_log2;
 
   f32x16 dq_acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) dq_acc[d] = f32x16{};
-  const int n_kt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
 
-  tile_dma(tiles[0][0], kbase, rs, 0, p.L, wv, lane);
-  tile_dma(tiles[0][1], vbase, rs, 0, p.L, wv, lane);
+  uint32_t roff[2], toff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    roff[c] = rowtile_lane_off<DQ_WAVES>(wv, c, lane);
+    toff[c] = ttile_lane_off<DQ_WAVES>(wv, c, lane);
+  }
+  const uint32_t bytes = (uint32_t)nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+  const __amdgpu_buffer_rsrc_t kfr = tile_rsrc(p.kf + tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t ktr = tile_rsrc(p.kt + tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t vrr = tile_rsrc(p.vr + tile0 * TILE_ELEMS, bytes);
+  const int* kexp = p.kexp + tile0;
+
+  auto stage = [&](int buf, int t) {
+    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      buf_dma16(kfr, roff[c], soff, tile_lds_block<DQ_WAVES>(tiles[buf][0], wv, c));
+      buf_dma16(ktr, toff[c], soff, tile_lds_block<DQ_WAVES>(tiles[buf][1], wv, c));
+      buf_dma16(vrr, roff[c], soff, tile_lds_block<DQ_WAVES>(tiles[buf][2], wv, c));
+    }
+  };
+
+  stage(0, 0);
+  int e_k = kexp[0];
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < n_kt; ++t) {
+  for (int t = 0; t < nt; ++t) {
     const int buf = t & 1;
-    const bool has_next = t + 1 < n_kt;
+    const bool has_next = t + 1 < nt;
+    int e_k_next = 0;
     if (has_next) {
-      tile_dma(tiles[buf ^ 1][0], kbase, rs, (t + 1) * TILE_ROWS, p.L, wv, lane);
-      tile_dma(tiles[buf ^ 1][1], vbase, rs, (t + 1) * TILE_ROWS, p.L, wv, lane);
+      stage(buf ^ 1, t + 1);
+      e_k_next = kexp[t + 1];
     }
     const uint16_t* ks = tiles[buf][0];
-    const uint16_t* vs = tiles[buf][1];
+    const uint16_t* kts = tiles[buf][1];
+    const uint16_t* vs = tiles[buf][2];
     const int key0 = t * TILE_ROWS;
     const bool partial = key0 + TILE_ROWS > p.L;
+    const float g = ldexpf(p.scale_log2, e_q + e_k);
 
     bf16x8 dsf[4];
 #pragma unroll
@@ -287,15 +301,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
-        s_acc = mfma32(a, qf[s], s_acc);
-        if (SPLIT) s_acc = mfma32(a, ql[s], s_acc);
+        s_acc = mfma32_f16(lds_row_frag(ks, kb * 32 + col, 2 * s + half), qf[s], s_acc);
         dp_acc = mfma32(lds_row_frag(vs, kb * 32 + col, 2 * s + half), dof[s], dp_acc);
       }
       float dsv[16];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], c2, -lse2));
+        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2));
         if (partial) {
           const int key = key0 + kb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
           if (key >= p.L) pe = 0.f;
@@ -309,18 +321,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg) {
-        dq_acc[d] = mfma32(lds_col_frag(ks, kg * 16, d * 32, lane), dsf[kg], dq_acc[d]);
+        dq_acc[d] = mfma32(lds_vt_frag(kts, d * 32 + col, kg, half), dsf[kg], dq_acc[d]);
       }
     }
 
     if (has_next) wait_vmem();
     __syncthreads();
+    e_k = e_k_next;
   }
 
   if (row_ok) {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr) pos = token_pos(p.rope, i);
-    uint16_t* dqrow = p.dq + head_off + (int64_t)i * rs;
+    const int64_t rs = (int64_t)p.H * HD;
+    uint16_t* dqrow = p.dq + ((int64_t)b * p.L * p.H + h) * HD + (int64_t)i * rs;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -333,33 +347,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_delta(const BwdParams& p, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.B * p.L * p.H * 16;
-  int64_t blocks = (threads + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+// The tiles of one (b, h) are addressed through buffer resources of 32-bit extent.
+bool tiles_addressable(int L) {
+  return (int64_t)((L + TILE_ROWS - 1) / TILE_ROWS) * (TILE_ELEMS * 2) <= (int64_t)0xffffffff;
 }
 
+}  // namespace
+
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
+  if (!tiles_addressable(p.L)) return hipErrorInvalidValue;
   BwdParams q = p;
   q.n_tiles = (p.L + 127) / 128;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  if (p.q_lo != nullptr) hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, q);
-  else hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)total), dim3(64 * DKDV_WAVES), 0, stream, q);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
+  if (!tiles_addressable(p.L)) return hipErrorInvalidValue;
   BwdParams q = p;
-  q.n_tiles = (p.L + 127) / 128;
+  q.n_tiles = (p.L + 255) / 256;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  if (p.q_lo != nullptr) hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, q);
-  else hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)total), dim3(64 * DQ_WAVES), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -13,10 +13,11 @@
 //    of S^T = K Q^T (bf16 MFMA 32x32x16), so every lane owns one query row and
 //    the softmax needs one cross-lane step (lane l <-> l^32) per tile;
 //  * F16 (with RoPE): the score product runs in fp16 (3 more mantissa bits
-//    than bf16, same MFMA rate).  The rotated query row is scaled by 2^-e_q
-//    so that its largest |element| lies in [2^14, 2^15) and rounded to fp16;
-//    the key pre-pass does the same per 64-key tile (exponent e_t); the
-//    softmax applies s = scale * 2^(e_q + e_t) * S.  Rounding the rotated
+//    than bf16, same MFMA rate).  Each 64-row tile of rotated queries is
+//    scaled by 2^-e_q so that its largest |element| lies in [2^14, 2^15) and
+//    rounded to fp16; the key pre-pass does the same per 64-key tile
+//    (exponent e_t); the softmax applies s = scale * 2^(e_q + e_t) * S.  The
+//    backward's prep passes reproduce these fp16 operands bit for bit.  Rounding the rotated
 //    query to bf16 instead would move LSE by up to ~1.2e-3 at 720p: a query's
 //    rounding error shifts all its scores coherently; in fp16 it is 8x
 //    smaller.  Without RoPE the inputs are used as given (bf16, exact);
@@ -50,6 +51,7 @@ constexpr float RESCALE_SLACK = 8.0f;     // log2 units: P stays <= 256 between 
 template <bool POS_SCALE, bool F16, bool TILED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE_ELEMS];   // [buffer][K|V]
+  __shared__ float qmax_s[FWD_WAVES];                                        // F16: max |q~| per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   const int i = qt * FWD_BR + wave * 32 + col;
   const bool row_ok = i < p.Lq;
   bf16x8 qf[8];       // F16: fp16 bit patterns
-  float g_q = p.scale_log2;   // score factor of this row: s * log2(e) = g_q * 2^e_t * S
+  float g_q = p.scale_log2;   // score factor of this wave: s * log2(e) = g_q * 2^e_t * S
   {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
@@ -100,7 +102,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
           mq = fmaxf(mq, fmaxf(fabsf(y0), fabsf(y1)));
         }
       }
-      const int e_q = pow2_exponent_15(xor32_max(mq));
+      // One exponent per 64-row query tile (waves 2u and 2u+1): the largest
+      // |q~| of the tile goes to [2^14, 2^15).
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mq = fmaxf(mq, __shfl_xor(mq, o));
+      if (lane == 0) qmax_s[wave] = mq;
+      __syncthreads();
+      const int e_q = pow2_exponent_15(fmaxf(qmax_s[wave & ~1], qmax_s[wave | 1]));
       g_q = ldexpf(p.scale_log2, e_q);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -219,8 +227,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     uint32_t koff[4], voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      koff[i] = ktile_lane_off(wv, i, lane);
-      voff[i] = rows128_lane_off<4>(wv, i, lane);
+      koff[i] = rowtile_lane_off<FWD_WAVES>(wv, i, lane);
+      voff[i] = ttile_lane_off<FWD_WAVES>(wv, i, lane);
     }
     const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(TILED ? p.kt + tile0 * TILE_ELEMS : p.k, bytes);
@@ -229,12 +237,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     auto stage = [&](int buf, int t) {
       if (TILED) {
         const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
-        uint8_t* kl = reinterpret_cast<uint8_t*>(smem[buf][0]) + 4096 * wv;
-        uint8_t* vl = reinterpret_cast<uint8_t*>(smem[buf][1]) + 4096 * wv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          buf_dma16(krs, koff[i], soff, kl + 1024 * i);
-          buf_dma16(vrs, voff[i], soff, vl + 1024 * i);
+          buf_dma16(krs, koff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][0], wv, i));
+          buf_dma16(vrs, voff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][1], wv, i));
         }
       } else {
         tile_dma(smem[buf][0], kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);

@@ -116,22 +116,6 @@ __device__ __forceinline__ u32x4 rope_chunk(const RopeDev& r, const TokenPos& p,
   return y;
 }
 
-// Same rotation, but the result is returned as a bf16 pair hi + lo with
-// hi = RNE(y) and lo = RNE(y - hi): together they carry ~16 significant bits,
-// so a product with them loses no more than a product with unrounded y would
-// to the second operand's own rounding.
-__device__ __forceinline__ void rope_chunk_split(const RopeDev& r, const TokenPos& p, int c, u32x4 x,
-                                                 u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float x0 = bf16_lo(x[t]);
-    float x1 = bf16_hi(x[t]);
-    rope_rotate(x0, x1, rope_cs(r, p, 4 * c + t), false);
-    const uint32_t h = pack_bf16(x0, x1);
-    hi[t] = h;
-    lo[t] = pack_bf16(x0 - bf16_lo(h), x1 - bf16_hi(h));
-  }
-}
 
 // ---------------------------------------------------------------------------
 // LDS tiles: 64 rows x 128 bf16, row-major, 256 bytes per row, no padding.
@@ -194,21 +178,28 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int tile8_off(int row, int chunk) { return row * 128 + ((chunk ^ swz8(row)) << 4); }
 
-// Staging from contiguous tiles (all rows present).  The per-lane byte
-// offsets do not depend on the tile, so they are computed once; lane l of a
-// 1 KB copy lands at byte 16*l of its LDS block.
-//   bf16 tile, 64 rows x 256 B, instruction i of wave w: rows 16w + 4i + l/16,
-//     logical chunk (l%16) ^ swz(row) (the layout of tile_dma);
-//   tile of 128-byte rows, instruction i of wave w with NI per wave: rows
-//     8*NI*w + 8i + l/8, logical chunk (l%8) ^ swz8(row).
-__device__ __forceinline__ uint32_t ktile_lane_off(int wave, int i, int lane) {
-  const int r = 16 * wave + 4 * i + (lane >> 4);
+// Staging from contiguous 16 KB tiles (all rows present) by NW waves: each
+// wave issues 16/NW copies of 1 KB; copy i of wave w fills LDS bytes
+// [(16384/NW)*w + 1024*i, +1024), lane l the 16 bytes at 16*l of that block.
+// The lane byte offsets into the tile do not depend on the tile, so they
+// are computed once.
+//   row tile (64 rows x 256 B): rows (64/NW)*w + 4i + l/16, logical chunk
+//     (l%16) ^ swz(row) (the layout of tile_dma);
+//   T tile (128 rows x 128 B): rows (128/NW)*w + 8i + l/8, logical chunk
+//     (l%8) ^ swz8(row).
+template <int NW>
+__device__ __forceinline__ uint32_t rowtile_lane_off(int wave, int i, int lane) {
+  const int r = (64 / NW) * wave + 4 * i + (lane >> 4);
   return (uint32_t)(r * 256 + (((lane & 15) ^ swz(r)) << 4));
 }
-template <int NI>
-__device__ __forceinline__ uint32_t rows128_lane_off(int wave, int i, int lane) {
-  const int r = 8 * NI * wave + 8 * i + (lane >> 3);
+template <int NW>
+__device__ __forceinline__ uint32_t ttile_lane_off(int wave, int i, int lane) {
+  const int r = (128 / NW) * wave + 8 * i + (lane >> 3);
   return (uint32_t)(r * 128 + (((lane & 7) ^ swz8(r)) << 4));
+}
+template <int NW>
+__device__ __forceinline__ uint8_t* tile_lds_block(void* lds_tile, int wave, int i) {
+  return reinterpret_cast<uint8_t*>(lds_tile) + (16384 / NW) * wave + 1024 * i;
 }
 // Raw buffer resource over `bytes` bytes at `base` (stride 0; dword 3 as for
 // gfx9 raw buffers).  Copies through it keep the per-tile step in the scalar

@@ -27,17 +27,21 @@ struct FwdParams {
   int n_qtiles;             // set by the launcher
 };
 
-// Self-attention backward.  All [B, L, H, 128] bf16 except lse/delta [B, H, L] fp32.
+// Self-attention backward over the prep passes' tiles: [B, H, ceil(L/64)]
+// tiles of 16 KB each (row tiles [64][128], T tiles [128][64]).
 struct BwdParams {
-  const uint16_t* q;        // rotated queries (bf16 hi part when q_lo != nullptr)
-  const uint16_t* q_lo;     // rotated queries, lo part (q - hi rounded to bf16), or nullptr
-  const uint16_t* k;        // rotated keys
-  const uint16_t* v;
-  const uint16_t* o;
-  const uint16_t* dout;
-  const float* lse;
-  float* delta;             // workspace [B, H, L]
-  uint16_t* dq;
+  const uint16_t* qf;       // Q row tiles, fp16 of R(p) q * 2^-e
+  const int* qexp;          // e of every Q tile
+  const uint16_t* qt;       // (R q)^T T tiles, bf16
+  const uint16_t* dor;      // dO row tiles, bf16
+  const uint16_t* dot;      // dO^T T tiles, bf16
+  const uint16_t* kf;       // K row tiles, fp16 of R(p) k * 2^-e
+  const int* kexp;          // e of every K tile
+  const uint16_t* kt;       // (R k)^T T tiles, bf16
+  const uint16_t* vr;       // V row tiles, bf16
+  const float* lse;         // [B, H, L]
+  const float* delta;       // [B, H, L]
+  uint16_t* dq;             // [B, L, H, 128] bf16 outputs
   uint16_t* dk;
   uint16_t* dv;
   RopeDev rope;             // rope.table != nullptr: rotate dq/dk back by minus the angle
@@ -51,12 +55,14 @@ hipError_t launch_rope_table(float* table, int f, int h, int w, int d_f, int d_h
                              hipStream_t stream);
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int B, int L, int H, const RopeDev& rope,
                          bool inverse, hipStream_t stream);
-hipError_t launch_rope3d_split(const uint16_t* x, uint16_t* hi, uint16_t* lo, int B, int L, int H,
-                               const RopeDev& rope, hipStream_t stream);
 hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, int* kexp, uint16_t* vt, int B, int L,
                            int H, const RopeDev& rope, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_delta(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
+                              uint16_t* vr, int B, int L, int H, const RopeDev& rope, hipStream_t stream);
+hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
+                              uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
+                              const RopeDev& rope, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 

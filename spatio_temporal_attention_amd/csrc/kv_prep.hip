@@ -1,18 +1,25 @@
-// Key/value preparation for the self-attention forward: one pass over K and V
-// that writes them in the forward's tile layout, so that its main loop stages
-// each 64-key tile with plain contiguous copies (no row clamping or 64-bit
-// address arithmetic per tile) and reads V without the LDS transpose.
+// Tile preparation passes.  The attention kernels stage 64-token tiles of
+// one (b, h) with contiguous copies and read every MFMA operand with plain
+// 16-byte LDS reads; these passes write the operands in that form, once:
 //
-// Per (b, h, tile t) of 64 keys k = 64t .. 64t+63 (keys >= L are zero):
-//   kt  [64][128]   without RoPE: the keys as given (bf16); with RoPE: the
-//                   keys rotated by 3D RoPE over the (frame, height, width)
-//                   token grid (Wan2.1 reading notes, 2. Model Design), in
-//                   fp32, scaled by 2^-e_t and rounded to fp16, where e_t
-//                   puts the tile's largest |element| in [2^14, 2^15);
-//   kexp[t]         e_t (with RoPE);
-//   vt  [128][64]   V transposed (bf16): row d holds v_k[d] at position
-//                   pos(k), pos = k with bits 2 and 3 swapped (the key order
-//                   of the PV product's register fragments).
+//   row tile  [64][128]  token-major, as the [B, L, H, 128] input row order;
+//   T tile    [128][64]  transposed: row d holds x_n[d] of the tile's tokens n
+//                        at position pos(n), pos = n with bits 2 and 3
+//                        swapped (the k order of the MFMA register fragments
+//                        that feed the products contracting over tokens);
+//   fp16 tile            a row tile of R(p) x * 2^-e, e chosen per tile so
+//                        that the largest |R(p) x| lies in [2^14, 2^15), and
+//                        the exponent e beside it.  R is the 3D RoPE over the
+//                        (frame, height, width) token grid (Wan2.1 reading
+//                        notes, 2. Model Design), or the identity.
+// Tokens >= L are zero in every tile.
+//
+// Forward (kv_tiles_kernel): K as an fp16 tile with its exponent (with RoPE)
+// or a bf16 row tile (without), V as a T tile.
+// Backward (bwd_k_tiles_kernel, bwd_q_tiles_kernel): the fp16 tiles of K and
+// Q with their exponents (bit-identical to what the forward multiplies, so
+// the recomputed scores match the forward's LSE), T tiles of R(p)k, R(p)q
+// and dO, row tiles of V and dO, and Delta_i = <dO_i, O_i>.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,73 +27,86 @@ namespace wanattn {
 
 namespace {
 
-template <bool F16>
-__global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                       uint16_t* __restrict__ kt, int* __restrict__ kexp,
-                                                       uint16_t* __restrict__ vt, int L, int H, int nt,
-                                                       RopeDev rope) {
-  __shared__ __attribute__((aligned(16))) uint16_t s[TILE_ROWS][HD + 8];
-  __shared__ float wmax[4];
-  const int tile = blockIdx.x % nt;
-  const int bh = blockIdx.x / nt;
-  const int h = bh % H;
-  const int b = bh / H;
-  const int tid = threadIdx.x;
-  const int64_t tile_elems = (int64_t)blockIdx.x * TILE_ELEMS;
-  float r[4][8];      // keys of this thread's 4 chunks (rotated with F16)
-  float mk = 0.f;
+// Thread t (of 256) holds tile tokens n = t/16 + 16*it at 8-element chunk
+// c = t%16, it = 0..3: each 16-lane group reads one 256-byte row.
+struct TileFrag {
+  float x[4][8];
+};
+
+__device__ __forceinline__ int frag_token(int tid, int it) { return (tid >> 4) + 16 * it; }
+__device__ __forceinline__ int frag_chunk(int tid) { return tid & 15; }
+
+// Load tokens [64*tile, +64) of head (b, h) of a [B, L, H, 128] bf16 tensor,
+// optionally rotated (fp32), and return this thread's max |x|.
+__device__ __forceinline__ float load_tile(TileFrag& f, const uint16_t* __restrict__ x, int b, int h, int tile, int L,
+                                           int H, const RopeDev* rope, int tid) {
+  float m = 0.f;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int c = tid + 256 * it;   // 64 keys x 16 chunks of 8 d
-    const int key = c >> 4;
-    const int ch = c & 15;
-    const int gk = tile * TILE_ROWS + key;
-    u32x4 kx = u32x4{0u, 0u, 0u, 0u};
-    u32x4 vx = u32x4{0u, 0u, 0u, 0u};
-    if (gk < L) {
-      const int64_t off = (((int64_t)b * L + gk) * H + h) * HD + ch * 8;
-      kx = *reinterpret_cast<const u32x4*>(k + off);
-      vx = *reinterpret_cast<const u32x4*>(v + off);
-    }
+    const int n = tile * TILE_ROWS + frag_token(tid, it);
+    const int ch = frag_chunk(tid);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (n < L) v = *reinterpret_cast<const u32x4*>(x + (((int64_t)b * L + n) * H + h) * HD + ch * 8);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      r[it][2 * t] = bf16_lo(kx[t]);
-      r[it][2 * t + 1] = bf16_hi(kx[t]);
+      f.x[it][2 * t] = bf16_lo(v[t]);
+      f.x[it][2 * t + 1] = bf16_hi(v[t]);
     }
-    if (F16 && gk < L) {
-      const TokenPos pos = token_pos(rope, gk);
+    if (rope != nullptr && n < L) {
+      const TokenPos pos = token_pos(*rope, n);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rope_rotate(r[it][2 * t], r[it][2 * t + 1], rope_cs(rope, pos, 4 * ch + t), false);
+      for (int t = 0; t < 4; ++t) rope_rotate(f.x[it][2 * t], f.x[it][2 * t + 1], rope_cs(*rope, pos, 4 * ch + t), false);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mk = fmaxf(mk, fabsf(r[it][e]));
-    *reinterpret_cast<u32x4*>(&s[key][ch * 8]) = vx;
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f.x[it][e]));
   }
-  int et = 0;
-  if (F16) {
-    // tile max |k~| -> e_t
+  return m;
+}
+
+// Max over the 256 threads (every thread gets it).  Ends with a barrier.
+__device__ __forceinline__ float block_max(float m, float* wmax, int tid) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mk = fmaxf(mk, __shfl_xor(mk, o));
-    if ((tid & 63) == 0) wmax[tid >> 6] = mk;
-  }
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
   __syncthreads();
-  if (F16) {
-    et = pow2_exponent_15(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
-    if (tid == 0) kexp[blockIdx.x] = et;
-  }
+  return fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+__device__ __forceinline__ void store_row_tile_f16(uint16_t* __restrict__ tile, const TileFrag& f, int e, int tid) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int c = tid + 256 * it;
-    const int key = c >> 4;
-    const int ch = c & 15;
-    u32x4 ko;
+    u32x4 w;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      ko[t] = F16 ? pack_f16(ldexpf(r[it][2 * t], -et), ldexpf(r[it][2 * t + 1], -et))
-                  : pack_bf16(r[it][2 * t], r[it][2 * t + 1]);
-    *reinterpret_cast<u32x4*>(kt + tile_elems + key * HD + ch * 8) = ko;
+    for (int t = 0; t < 4; ++t) w[t] = pack_f16(ldexpf(f.x[it][2 * t], -e), ldexpf(f.x[it][2 * t + 1], -e));
+    *reinterpret_cast<u32x4*>(tile + frag_token(tid, it) * HD + frag_chunk(tid) * 8) = w;
   }
-  uint16_t* out = vt + tile_elems;
+}
+
+__device__ __forceinline__ void store_row_tile_bf16(uint16_t* __restrict__ tile, const TileFrag& f, int tid) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    u32x4 w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t] = pack_bf16(f.x[it][2 * t], f.x[it][2 * t + 1]);
+    *reinterpret_cast<u32x4*>(tile + frag_token(tid, it) * HD + frag_chunk(tid) * 8) = w;
+  }
+}
+
+typedef uint16_t StageRows[TILE_ROWS][HD + 8];   // padded: column reads spread over banks
+
+// bf16 of the fragment into the LDS staging rows (no barrier).
+__device__ __forceinline__ void stage_bf16(StageRows& s, const TileFrag& f, int tid) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    u32x4 w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t] = pack_bf16(f.x[it][2 * t], f.x[it][2 * t + 1]);
+    *reinterpret_cast<u32x4*>(&s[frag_token(tid, it)][frag_chunk(tid) * 8]) = w;
+  }
+}
+
+// T tile from the staged rows (call after a barrier).
+__device__ __forceinline__ void store_t_tile(uint16_t* __restrict__ tile, const StageRows& s, int tid) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int c = tid + 256 * it;   // 128 d rows x 8 chunks of 8 positions
@@ -96,28 +116,157 @@ __global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restric
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int p0 = 8 * pc + 2 * e;
-      const int k0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);   // bit 0 untouched: k0 + 1 is p0 + 1
-      w[e] = (uint32_t)s[k0][d] | ((uint32_t)s[k0 + 1][d] << 16);
+      const int n0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);   // bit 0 untouched: n0 + 1 is p0 + 1
+      w[e] = (uint32_t)s[n0][d] | ((uint32_t)s[n0 + 1][d] << 16);
     }
-    *reinterpret_cast<u32x4*>(out + d * 64 + pc * 8) = w;
+    *reinterpret_cast<u32x4*>(tile + d * 64 + pc * 8) = w;
   }
+}
+
+// Forward: K (fp16 tile + exponent with RoPE, bf16 row tile without) and V^T.
+template <bool F16>
+__global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                       uint16_t* __restrict__ kt, int* __restrict__ kexp,
+                                                       uint16_t* __restrict__ vt, int L, int H, int nt,
+                                                       RopeDev rope) {
+  __shared__ __attribute__((aligned(16))) StageRows s;
+  __shared__ float wmax[4];
+  const int tile = blockIdx.x % nt;
+  const int bh = blockIdx.x / nt;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int tid = threadIdx.x;
+  const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
+  TileFrag f;
+  const float mk = load_tile(f, k, b, h, tile, L, H, F16 ? &rope : nullptr, tid);
+  if (F16) {
+    const int e = pow2_exponent_15(block_max(mk, wmax, tid));
+    if (tid == 0) kexp[blockIdx.x] = e;
+    store_row_tile_f16(kt + off, f, e, tid);
+  } else {
+    store_row_tile_bf16(kt + off, f, tid);
+  }
+  load_tile(f, v, b, h, tile, L, H, nullptr, tid);
+  stage_bf16(s, f, tid);
+  __syncthreads();
+  store_t_tile(vt + off, s, tid);
+}
+
+// Backward, key side: K fp16 tile + exponent (as the forward's), (R k)^T, V rows.
+__global__ __launch_bounds__(256) void bwd_k_tiles_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, uint16_t* __restrict__ kf,
+                                                          int* __restrict__ kexp, uint16_t* __restrict__ kt,
+                                                          uint16_t* __restrict__ vr, int L, int H, int nt,
+                                                          RopeDev rope) {
+  __shared__ __attribute__((aligned(16))) StageRows s;
+  __shared__ float wmax[4];
+  const int tile = blockIdx.x % nt;
+  const int bh = blockIdx.x / nt;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int tid = threadIdx.x;
+  const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
+  TileFrag f;
+  const float mk = load_tile(f, k, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid);
+  const int e = pow2_exponent_15(block_max(mk, wmax, tid));
+  if (tid == 0) kexp[blockIdx.x] = e;
+  store_row_tile_f16(kf + off, f, e, tid);
+  stage_bf16(s, f, tid);
+  __syncthreads();
+  store_t_tile(kt + off, s, tid);
+  load_tile(f, v, b, h, tile, L, H, nullptr, tid);
+  store_row_tile_bf16(vr + off, f, tid);
+}
+
+// Backward, query side: Q fp16 tile + exponent, (R q)^T, dO rows, dO^T, Delta.
+__global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ dout,
+                                                          const uint16_t* __restrict__ o, uint16_t* __restrict__ qf,
+                                                          int* __restrict__ qexp, uint16_t* __restrict__ qt,
+                                                          uint16_t* __restrict__ dor, uint16_t* __restrict__ dot,
+                                                          float* __restrict__ delta, int L, int H, int nt,
+                                                          RopeDev rope) {
+  __shared__ __attribute__((aligned(16))) StageRows s;
+  __shared__ float wmax[4];
+  const int tile = blockIdx.x % nt;
+  const int bh = blockIdx.x / nt;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int tid = threadIdx.x;
+  const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
+  TileFrag f;
+  const float mq = load_tile(f, q, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid);
+  const int e = pow2_exponent_15(block_max(mq, wmax, tid));
+  if (tid == 0) qexp[blockIdx.x] = e;
+  store_row_tile_f16(qf + off, f, e, tid);
+  stage_bf16(s, f, tid);
+  __syncthreads();
+  store_t_tile(qt + off, s, tid);
+  __syncthreads();   // the staging rows are reused below
+
+  // dO: row tile, T tile, and Delta = <dO, O> per token (16 lanes per row).
+  load_tile(f, dout, b, h, tile, L, H, nullptr, tid);
+  store_row_tile_bf16(dor + off, f, tid);
+  stage_bf16(s, f, tid);
+  TileFrag g;
+  load_tile(g, o, b, h, tile, L, H, nullptr, tid);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    float d = 0.f;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) d = fmaf(f.x[it][e2], g.x[it][e2], d);
+    d += __shfl_xor(d, 8, 16);
+    d += __shfl_xor(d, 4, 16);
+    d += __shfl_xor(d, 2, 16);
+    d += __shfl_xor(d, 1, 16);
+    const int n = tile * TILE_ROWS + frag_token(tid, it);
+    if (frag_chunk(tid) == 0 && n < L) delta[((int64_t)b * H + h) * L + n] = d;
+  }
+  __syncthreads();
+  store_t_tile(dot + off, s, tid);
+}
+
+hipError_t grid_of_tiles(int B, int L, int H, int& nt, dim3& grid) {
+  nt = (L + TILE_ROWS - 1) / TILE_ROWS;
+  const int64_t total = (int64_t)B * H * nt;
+  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+  grid = dim3((unsigned)total);
+  return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, int* kexp, uint16_t* vt, int B, int L,
                            int H, const RopeDev& rope, hipStream_t stream) {
-  const int nt = (L + TILE_ROWS - 1) / TILE_ROWS;
-  const int64_t total = (int64_t)B * H * nt;
-  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+  int nt;
+  dim3 grid;
+  if (grid_of_tiles(B, L, H, nt, grid) != hipSuccess) return hipErrorInvalidValue;
   const bool f16 = rope.table != nullptr;
   if (f16 != (kexp != nullptr)) return hipErrorInvalidValue;
   if (f16)
-    hipLaunchKernelGGL(kv_tiles_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt,
-                       rope);
+    hipLaunchKernelGGL(kv_tiles_kernel<true>, grid, dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt, rope);
   else
-    hipLaunchKernelGGL(kv_tiles_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, k, v, kt, kexp, vt, L, H,
-                       nt, rope);
+    hipLaunchKernelGGL(kv_tiles_kernel<false>, grid, dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt, rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
+                              uint16_t* vr, int B, int L, int H, const RopeDev& rope, hipStream_t stream) {
+  int nt;
+  dim3 grid;
+  if (grid_of_tiles(B, L, H, nt, grid) != hipSuccess) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_k_tiles_kernel, grid, dim3(256), 0, stream, k, v, kf, kexp, kt, vr, L, H, nt, rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
+                              uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
+                              const RopeDev& rope, hipStream_t stream) {
+  int nt;
+  dim3 grid;
+  if (grid_of_tiles(B, L, H, nt, grid) != hipSuccess) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_q_tiles_kernel, grid, dim3(256), 0, stream, q, dout, o, qf, qexp, qt, dor, dot, delta, L, H,
+                     nt, rope);
   return hipGetLastError();
 }
 

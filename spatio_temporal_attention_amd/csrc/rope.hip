@@ -54,34 +54,7 @@ __global__ __launch_bounds__(256) void rope3d_kernel(const uint16_t* x, uint16_t
   }
 }
 
-// Rotation to a bf16 hi + lo pair (hi = RNE(y), lo = RNE(y - hi)).
-__global__ __launch_bounds__(256) void rope3d_split_kernel(const uint16_t* x, uint16_t* hi, uint16_t* lo,
-                                                           int64_t nchunks, int L, int H, RopeDev rope) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t cidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; cidx < nchunks; cidx += stride) {
-    const int c = (int)(cidx & 15);
-    const int64_t row = cidx >> 4;
-    const int n = (int)((row / H) % L);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x + cidx * 8);
-    u32x4 h, l;
-    rope_chunk_split(rope, token_pos(rope, n), c, v, h, l);
-    *reinterpret_cast<u32x4*>(hi + cidx * 8) = h;
-    *reinterpret_cast<u32x4*>(lo + cidx * 8) = l;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_rope3d_split(const uint16_t* x, uint16_t* hi, uint16_t* lo, int B, int L, int H,
-                               const RopeDev& rope, hipStream_t stream) {
-  const int64_t nchunks = (int64_t)B * L * H * (HD / 8);
-  if (nchunks == 0) return hipSuccess;
-  int64_t blocks = (nchunks + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(rope3d_split_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, hi, lo, nchunks, L, H,
-                     rope);
-  return hipGetLastError();
-}
 
 hipError_t launch_rope_table(float* table, int f, int h, int w, int d_f, int d_h, int d_w, double theta,
                              hipStream_t stream) {

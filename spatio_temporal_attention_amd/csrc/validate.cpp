@@ -62,12 +62,29 @@ size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
   return self_fwd_ws_layout(B, L, H, D, with_rope).total;
 }
 
+BwdWsLayout self_bwd_ws_layout(int B, int L, int H, int D) {
+  BwdWsLayout w{};
+  if (check_dims(B, L, H, D) != WANATTN_OK) return w;
+  const size_t tiles = (size_t)B * H * (((size_t)L + 63) / 64);
+  const size_t tile_bytes = tiles * 64 * (size_t)D * 2;
+  size_t at = 0;
+  w.delta = at;
+  at = align256(at + (size_t)B * H * L * 4);
+  size_t* parts[] = {&w.qf, &w.qt, &w.dor, &w.dot, &w.kf, &w.kt, &w.vr};
+  for (size_t* part : parts) {
+    *part = at;
+    at = align256(at + tile_bytes);
+  }
+  w.qexp = at;
+  at = align256(at + tiles * 4);
+  w.kexp = at;
+  w.total = at + tiles * 4;
+  return w;
+}
+
 size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
-  if (check_dims(B, L, H, D) != WANATTN_OK) return 0;
-  size_t delta = (size_t)B * H * L * 4;
-  delta = (delta + 255) & ~(size_t)255;
-  if (!with_rope) return delta;
-  return delta + 3 * (size_t)B * L * H * D * 2;   // + rotated queries (hi, lo) and keys
+  (void)with_rope;   // the same tiles serve both
+  return self_bwd_ws_layout(B, L, H, D).total;
 }
 
 static int check_bf16(const void* p) {

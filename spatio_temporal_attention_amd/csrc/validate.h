@@ -29,6 +29,13 @@ struct FwdWsLayout {
 };
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope);
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);
+// Backward workspace: Delta (fp32 [B, H, L]), then the prep passes' tiles
+// (each [B, H, ceil(L/64)] x 16 KB) and the two exponent arrays (int32 per
+// tile); each part starts on a 256-byte boundary.
+struct BwdWsLayout {
+  size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, total;
+};
+BwdWsLayout self_bwd_ws_layout(int B, int L, int H, int D);
 size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope);
 
 int validate_rope3d(const void* x, const void* y, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,

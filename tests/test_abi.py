@@ -69,8 +69,10 @@ def test_workspace_sizes(lib):
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + 4 * n_tiles  # + tile exponents
     assert lib.wanattn_self_fwd_workspace_bytes(1, 1, 1, D, 0) == 2 * 64 * D * 2
     delta = (B * H * L * 4 + 255) // 256 * 256
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 3 * B * L * H * D * 2
+    exps = (4 * n_tiles + 255) // 256 * 256 + 4 * n_tiles
+    # Delta, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 7 * tiled * 2 + exps
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta + 7 * tiled * 2 + exps
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, 64, 1) == 0
 
 
