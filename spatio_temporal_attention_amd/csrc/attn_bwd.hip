@@ -26,6 +26,8 @@
 //  * bwd_dq:   workgroup = 256 queries (8 waves, two per SIMD), loop over
 //    64-key tiles staged as K fp16 rows, (R k)^T, V rows.  S^T = K Q^T,
 //    dP^T = V dO^T (lane owns query i), dQ~^T += (R k)^T dS^T.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -280,21 +282,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < nt;
-    int e_k_next = 0;
-    if (has_next) {
-      stage(buf ^ 1, t + 1);
-      e_k_next = kexp[t + 1];
-    }
+  // One 64-key tile; MASK: the last tile when L % 64 != 0 (keys >= L get P = 0).
+  auto key_tile = [&](auto mask_tag, int t, int buf) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* ks = tiles[buf][0];
     const uint16_t* kts = tiles[buf][1];
     const uint16_t* vs = tiles[buf][2];
-    const int key0 = t * TILE_ROWS;
-    const bool partial = key0 + TILE_ROWS > p.L;
     const float g = ldexpf(p.scale_log2, e_q + e_k);
-
     bf16x8 dsf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -308,8 +302,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2));
-        if (partial) {
-          const int key = key0 + kb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
+        if (MASK) {
+          const int key = t * TILE_ROWS + kb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
           if (key >= p.L) pe = 0.f;
         }
         dsv[jj] = pe * (dp_acc[jj] - delta);
@@ -324,11 +318,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         dq_acc[d] = mfma32(lds_vt_frag(kts, d * 32 + col, kg, half), dsf[kg], dq_acc[d]);
       }
     }
+  };
 
+  // Full tiles in the loop; a partial last tile is peeled off after it.
+  const int n_full = p.L / TILE_ROWS;
+  for (int t = 0; t < n_full; ++t) {
+    const int buf = t & 1;
+    const bool has_next = t + 1 < nt;
+    int e_k_next = 0;
+    if (has_next) {
+      stage(buf ^ 1, t + 1);
+      e_k_next = kexp[t + 1];
+    }
+    key_tile(std::false_type{}, t, buf);
     if (has_next) wait_vmem();
     __syncthreads();
     e_k = e_k_next;
   }
+  if (n_full < nt) key_tile(std::true_type{}, n_full, n_full & 1);
 
   if (row_ok) {
     TokenPos pos{0, 0, 0};
