@@ -140,14 +140,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 
-  // One 64-key tile: scores, online softmax, O += P V.  MASK: the last tile,
-  // whose keys past n_keys get -inf (full tiles carry no masking code).
-  auto tile_step = [&](auto mask_tag, const uint16_t* ks, const uint16_t* vs, int t, int e_t) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // log2-domain factor of this tile's raw scores
-    const float g = F16 ? ldexpf(g_q, e_t) : g_q;
-    // S^T (64 keys x 32 queries) as two 32x32 blocks.
-    f32x16 s_acc[2];
+  // S^T of one 64-key tile (64 keys x 32 queries) as two 32x32 blocks.
+  auto scores = [&](const uint16_t* ks, f32x16 (&s_acc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s_acc[kb] = f32x16{};
@@ -157,6 +151,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
         s_acc[kb] = F16 ? mfma32_f16(a, qf[s], s_acc[kb]) : mfma32(a, qf[s], s_acc[kb]);
       }
     }
+  };
+
+  // Online softmax of tile t's scores and O += P V.  MASK: the last tile,
+  // whose keys past n_keys get -inf (full tiles carry no masking code).
+  // NEXT: also compute the next tile's scores (from next_ks into s_nxt) in
+  // the same basic block as this tile's exponentials (after the rescale
+  // branch), so the scheduler can interleave them: one wave issues in
+  // order, and the MFMAs only overlap VALU work placed between them.
+  auto softmax_pv = [&](auto mask_tag, auto next_tag, f32x16 (&s_acc)[2], const uint16_t* vs, int t, int e_t,
+                        const uint16_t* next_ks, f32x16 (&s_nxt)[2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+    // log2-domain factor of this tile's raw scores
+    const float g = F16 ? ldexpf(g_q, e_t) : g_q;
 
     // Scores: raw for a positive scale, otherwise already scaled to the log2 domain.
     float sv[2][16];
@@ -192,6 +200,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
     }
+
+    if (NEXT) scores(next_ks, s_nxt);
 
     // P in bf16 (RNE) for PV; l sums P in fp32 (summing the rounded values
     // instead would move LSE by up to ~2^-9 when few keys dominate).
@@ -233,43 +243,65 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(TILED ? p.kt + tile0 * TILE_ELEMS : p.k, bytes);
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(TILED ? p.vt + tile0 * TILE_ELEMS : p.v, bytes);
-    // Stage tile t of K and V into buffer `buf`.
-    auto stage = [&](int buf, int t) {
+    // Stage tile t of K (V) into K (V) buffer `buf`.
+    auto stage_k = [&](int buf, int t) {
       if (TILED) {
         const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          buf_dma16(krs, koff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][0], wv, i));
-          buf_dma16(vrs, voff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][1], wv, i));
-        }
+        for (int i = 0; i < 4; ++i) buf_dma16(krs, koff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][0], wv, i));
       } else {
         tile_dma(smem[buf][0], kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
+      }
+    };
+    auto stage_v = [&](int buf, int t) {
+      if (TILED) {
+        const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf_dma16(vrs, voff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][1], wv, i));
+      } else {
         tile_dma(smem[buf][1], vbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
       }
     };
-    // A tile's exponent is loaded with its copies, so the wait that ends the
-    // previous tile covers it.
-    stage(0, 0);
+    // Software pipeline: iteration t computes the scores of tile t+1 (MFMA)
+    // while the softmax of tile t (VALU) runs, then O += P(t) V(t).  K runs
+    // one tile ahead of V: iteration t copies K(t+2) and V(t+1) into the
+    // buffers K(t) and V(t-1) have left.  A tile's exponent is loaded with
+    // its copies, so the wait that ends the previous iteration covers it.
+    stage_k(0, 0);
+    stage_v(0, 0);
     int e_cur = F16 ? kexp[0] : 0;
+    int e_nxt = 0;
+    if (n_tiles > 1) {
+      stage_k(1, 1);
+      if (F16) e_nxt = kexp[1];
+    }
     wait_vmem();
     __syncthreads();
-    // Full tiles in the loop; a partial last tile is peeled off after it.
-    const int n_full = n_keys / FWD_BC;
-    for (int t = 0; t < n_full; ++t) {
-      const int buf = t & 1;
-      const bool has_next = t + 1 < n_tiles;
-      int e_next = 0;
-      if (has_next) {
-        stage(buf ^ 1, t + 1);
-        if (F16) e_next = kexp[t + 1];
+    f32x16 s_cur[2];
+    scores(smem[0][0], s_cur);
+    __syncthreads();   // K buffer 0 is refilled in iteration 0
+    const int last = n_tiles - 1;
+    for (int t = 0; t < last; ++t) {
+      int e_nxt2 = 0;
+      if (t + 2 < n_tiles) {
+        stage_k(t & 1, t + 2);
+        if (F16) e_nxt2 = kexp[t + 2];
       }
-      tile_step(std::false_type{}, smem[buf][0], smem[buf][1], t, e_cur);
-      if (has_next) wait_vmem();
+      stage_v((t + 1) & 1, t + 1);
+      f32x16 s_nxt[2];
+      softmax_pv(std::false_type{}, std::true_type{}, s_cur, smem[t & 1][1], t, e_cur, smem[(t + 1) & 1][0], s_nxt);
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
+      e_cur = e_nxt;
+      e_nxt = e_nxt2;
+      wait_vmem();
       __syncthreads();
-      e_cur = e_next;
     }
-    if (n_full < n_tiles)
-      tile_step(std::true_type{}, smem[n_full & 1][0], smem[n_full & 1][1], n_full, e_cur);
+    // Only the last tile can be partial.
+    if (n_keys % FWD_BC != 0)
+      softmax_pv(std::true_type{}, std::false_type{}, s_cur, smem[last & 1][1], last, e_cur, nullptr, s_cur);
+    else
+      softmax_pv(std::false_type{}, std::false_type{}, s_cur, smem[last & 1][1], last, e_cur, nullptr, s_cur);
   }
 
   // ---- epilogue: O = O / l (bf16), LSE = ln sum exp(s) = ln2 * (m + log2 l)
