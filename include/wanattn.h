@@ -146,9 +146,12 @@ int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float
  *   dS_ij = P_ij (<dout_i, v_j> - Delta_i);
  *   dq_i = R(p_i)^T scale sum_j dS_ij R(p_j) k_j;  dk_j = R(p_j)^T scale sum_i dS_ij R(p_i) q_i.
  * Gradients are with respect to the unrotated q and k.  table == NULL: no RoPE.
- * Workspace: wanattn_self_bwd_workspace_bytes bytes (Delta fp32 [B, H, L], and
- * with a table the rotated q as a bf16 hi/lo pair and the rotated k, three
- * bf16 [B, L, H, D] tensors).
+ * Workspace (required, 16-byte aligned): wanattn_self_bwd_workspace_bytes bytes
+ * (the same with or without a table).  It receives Delta (fp32 [B, H, L]) and
+ * 64-token tiles of every (b, h): q and k (rotated with a table) in fp16 with
+ * the forward's per-tile powers of two, their bf16 transposes, dout (rows and
+ * transposed) and v, so that P is recomputed from exactly the operands the
+ * forward multiplied.  Its contents on return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 
@@ -158,6 +161,56 @@ int wanattn_self_bwd(const void* q, const void* k, const void* v, const void* o,
                      int B, int L, int H, int D,
                      wanattn_grid g, wanattn_rope r, const float* table, float scale,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Variable-length self-attention forward: batch item b holds seq_lens[b]
+ * valid tokens, the first ones of the [B, L, H, D] rows, and attends only
+ * among them ([notes] code notes, WanModel forward and the sampler both take
+ * a seq_len; [notes] 3. Training: joint image + video batches mix 1-frame and
+ * many-frame latents).  seq_lens: device int32 [B], each clamped to [0, L].
+ * Query rows i >= seq_lens[b] of o and lse are not written; keys
+ * j >= seq_lens[b] are never used (their contents may be anything).  RoPE
+ * positions follow the grid g of the padded length L (f*h*w == L), so a
+ * prefix of whole frames has the positions it would have in a sequence of
+ * its own.  Equal, item by item, to wanattn_self_fwd on the valid prefix.
+ * Workspace: wanattn_self_fwd_workspace_bytes(B, L, H, D, table != NULL).
+ * ------------------------------------------------------------------------- */
+int wanattn_self_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* seq_lens, int B, int L, int H, int D,
+                            wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Partial self-attention of one query shard over one key/value shard: the
+ * per-hop step of Ring attention, the key-sharded ("outside") half of the 2D
+ * context parallelism ([lit619] Key takeaways, attention dominates).  q holds
+ * tokens [q_offset, q_offset + Lq) and k, v tokens [k_offset, k_offset + Lk)
+ * of one sequence whose token grid is g (f*h*w >= both ends; RoPE positions
+ * are those of the global token indices).  o ([B, Lq, H, D]) and lse
+ * ([B, H, Lq], may be NULL) are the attention of the shard's queries over the
+ * shard's keys only; wanattn_lse_merge combines the shards exactly.  table ==
+ * NULL: no rotation (g and the offsets only need to be >= 0).
+ * Workspace: wanattn_partial_fwd_workspace_bytes(B, Lk, H, D, table != NULL).
+ * ------------------------------------------------------------------------- */
+size_t wanattn_partial_fwd_workspace_bytes(int B, int Lk, int H, int D, int with_rope);
+
+int wanattn_partial_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Lq, int Lk, int H, int D,
+                        wanattn_grid g, wanattn_rope r, const float* table,
+                        int q_offset, int k_offset, float scale,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Exact merge of R partial results over disjoint key sets (same source):
+ *   LSE = ln sum_r exp(LSE_r),  O = sum_r exp(LSE_r - LSE) O_r.
+ * o_parts, lse_parts: host arrays of R (1..16) device pointers to [B, L, H, D]
+ * bf16 and [B, H, L] fp32 partials; o: [B, L, H, D] bf16 out; lse: [B, H, L]
+ * fp32 out or NULL.  Parts with LSE_r = -inf (no keys) get weight 0; if all
+ * are -inf, O = 0 and LSE = -inf.  o may alias o_parts[0] (each element is
+ * read before it is written, by the same thread).
+ * ------------------------------------------------------------------------- */
+int wanattn_lse_merge(const void* const* o_parts, const float* const* lse_parts, int R,
+                      void* o, float* lse, int B, int L, int H, int D, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Cross-attention forward: video-token queries over text-token keys and values

@@ -31,6 +31,9 @@ from .reference import (  # noqa: F401
     rope3d_ref,
     attention_rows_ref,
     self_fwd_ref,
+    self_fwd_varlen_ref,
+    partial_fwd_ref,
+    lse_merge_ref,
     cross_fwd_ref,
     self_bwd_ref,
     cross_bwd_ref,

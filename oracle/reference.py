@@ -248,6 +248,94 @@ def cross_fwd_ref(q, k, v, k_lens, scale: float, rows=None):
 # Attention backward (standard calculus of the forward above)
 # ----------------------------------------------------------------------------
 
+def self_fwd_varlen_ref(q, k, v, seq_lens, scale: float, grid=None, rope: RopeSpec | None = None):
+    """Self-attention of each batch item over its first seq_lens[b] tokens only.
+
+    q, k, v: [B, L, H, D]; seq_lens: [B] ints, clamped to [0, L].  Positions
+    for RoPE are those of the padded grid (row-major, f*h*w == L), so a
+    prefix of whole frames keeps the positions it has in a sequence of its
+    own.  Returns O [B, L, H, D] and LSE [B, H, L] with NaN in the rows past
+    an item's length (those rows are not defined by the operation).
+    Joint image + video batches and the seq_len argument: Wan2.1 reading
+    notes, 3. Training and the code notes (WanModel forward, sampler).
+    Pinned in tests/test_oracle_shards.py (item = separate self-attention
+    call; full lengths = self_fwd_ref).
+    """
+    B, L, H, D = q.shape
+    o = np.full((B, L, H, D), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    for b in range(B):
+        n = int(min(max(int(seq_lens[b]), 0), L))
+        if n == 0:
+            continue
+        idx = np.arange(n)
+        for h in range(H):
+            kt = _rotated(k[b, :n, h, :], idx, grid, rope)
+            qt = _rotated(q[b, :n, h, :], idx, grid, rope)
+            ob, lb = attention_rows_ref(qt, kt, np.asarray(v[b, :n, h, :], dtype=np.float64), scale)
+            o[b, :n, h, :] = ob
+            lse[b, h, :n] = lb
+    return o, lse
+
+
+def partial_fwd_ref(q, k, v, scale: float, q_offset: int, k_offset: int, grid=None, rope: RopeSpec | None = None,
+                    rows=None):
+    """Attention of a query shard over a key/value shard of one longer sequence.
+
+    q: [B, Lq, H, D] holds global tokens q_offset .. q_offset+Lq-1, k and v
+    [B, Lk, H, D] tokens k_offset .. k_offset+Lk-1 of the sequence whose
+    token grid is `grid`; RoPE uses the global positions.  Returns the
+    shard-local O [B, Lq, H, D] and LSE [B, H, Lq] (or, with rows [B, H, R]
+    of local query indices, O [B, H, R, D] and LSE [B, H, R]).  The per-hop
+    step of Ring attention (anthology note, Key takeaways: Ring outside,
+    Ulysses inside).  Pinned in tests/test_oracle_shards.py.
+    """
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    if rope is not None and (q_offset + Lq > int(np.prod(grid)) or k_offset + Lk > int(np.prod(grid))):
+        raise ValueError("shard past the end of the grid")
+    qidx_all = q_offset + np.arange(Lq)
+    kidx = k_offset + np.arange(Lk)
+    if rows is None:
+        o = np.empty((B, Lq, H, D))
+        lse = np.empty((B, H, Lq))
+    else:
+        o = np.empty((B, H, rows.shape[2], D))
+        lse = np.empty((B, H, rows.shape[2]))
+    for b in range(B):
+        for h in range(H):
+            kt = _rotated(k[b, :, h, :], kidx, grid, rope)
+            loc = np.arange(Lq) if rows is None else rows[b, h]
+            qt = _rotated(q[b, loc, h, :], qidx_all[loc], grid, rope)
+            ob, lb = attention_rows_ref(qt, kt, np.asarray(v[b, :, h, :], dtype=np.float64), scale)
+            if rows is None:
+                o[b, :, h, :] = ob
+                lse[b, h] = lb
+            else:
+                o[b, h] = ob
+                lse[b, h] = lb
+    return o, lse
+
+
+def lse_merge_ref(o_parts, lse_parts):
+    """Merge partial results over disjoint key sets: LSE = ln sum_r exp(LSE_r),
+    O = sum_r exp(LSE_r - LSE) O_r.  o_parts: list of [B, L, H, D] arrays,
+    lse_parts: list of [B, H, L].  Rows where every LSE_r is -inf get O = 0 and
+    LSE = -inf.  Pinned in tests/test_oracle_shards.py (merging the shards of
+    a key split reproduces the unsplit attention)."""
+    lse_st = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])      # [R, B, H, L]
+    m = lse_st.max(axis=0)
+    safe_m = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(divide="ignore"):          # log(0) only where every part is empty
+        tot = np.log(np.exp(lse_st - safe_m).sum(axis=0)) + safe_m
+    tot = np.where(np.isfinite(m), tot, -np.inf)
+    w = np.where(np.isfinite(m), np.exp(lse_st - np.where(np.isfinite(tot), tot, 0.0)), 0.0)   # [R, B, H, L]
+    o = np.zeros(np.asarray(o_parts[0]).shape)
+    for r, op in enumerate(o_parts):
+        o += np.asarray(op, dtype=np.float64) * np.transpose(w[r], (0, 2, 1))[..., None]
+    return o, tot
+
+
 def _head_bwd(qt, kt, v, dout, scale):
     """Gradients of sum(dout * O) w.r.t. the rotated qt, kt and v of one head (full L x N)."""
     if kt.shape[0] == 0:

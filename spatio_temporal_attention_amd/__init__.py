@@ -67,6 +67,12 @@ _SIGNATURES = {
     "wanattn_self_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, Grid, Rope, _vp, _f,
                               _vp, _sz, _vp]),
     "wanattn_cross_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "wanattn_self_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, Grid, Rope, _vp, _f, _vp, _sz,
+                                     _vp]),
+    "wanattn_partial_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "wanattn_partial_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, Grid, Rope, _vp, _i, _i, _f, _vp, _sz,
+                                 _vp]),
+    "wanattn_lse_merge": (_i, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _vp, _vp, _i, _i, _i, _i, _vp]),
 }
 
 _LIB = None
@@ -263,4 +269,86 @@ def cross_fwd(q, k, v, k_lens=None, scale=None, out=None, lse=None, want_lse=Tru
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib().wanattn_cross_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(k_lens), _ptr(o), _ptr(lse), B, Lq, Lk, H, D,
                                    scale, _stream(q.device)))
+    return o, lse
+
+
+def self_fwd_varlen(q, k, v, seq_lens, grid=None, table=None, rope=None, scale=None, out=None, lse=None,
+                    workspace=None, want_lse=True):
+    """Self-attention forward where item b uses only its first seq_lens[b] tokens.  Returns (o, lse);
+    rows past an item's length are left as they were in `out` / `lse`."""
+    torch = _torch()
+    _need(q, torch.bfloat16, "q")
+    B, L, H, D = q.shape
+    _need(k, torch.bfloat16, "k", q.shape)
+    _need(v, torch.bfloat16, "v", q.shape)
+    _need(seq_lens, torch.int32, "seq_lens", (B,))
+    if table is not None:
+        _need(table, torch.float32, "table")
+    o = torch.zeros_like(q) if out is None else out
+    _need(o, torch.bfloat16, "out", q.shape)
+    if lse is None and want_lse:
+        lse = torch.zeros((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (B, H, L))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = self_fwd_workspace_bytes(B, L, H, D, table is not None)
+    ws = _workspace(nbytes, q.device, workspace)
+    g = _grid(grid if grid is not None else (1, 1, L))
+    _check(lib().wanattn_self_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(seq_lens), B, L, H, D,
+                                         g, _rope(rope), _ptr(table), scale, _ptr(ws),
+                                         nbytes if ws is None else ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def partial_fwd_workspace_bytes(B, Lk, H, D=HEAD_DIM, with_rope=True) -> int:
+    return int(lib().wanattn_partial_fwd_workspace_bytes(B, Lk, H, D, 1 if with_rope else 0))
+
+
+def partial_fwd(q, k, v, q_offset, k_offset, grid=None, table=None, rope=None, scale=None, out=None, lse=None,
+                workspace=None):
+    """Attention of a query shard (global tokens q_offset ...) over a key/value shard (k_offset ...) of one
+    sequence on token grid `grid`.  Returns (o, lse), the partial result for wanattn_lse_merge."""
+    torch = _torch()
+    _need(q, torch.bfloat16, "q")
+    B, Lq, H, D = q.shape
+    _need(k, torch.bfloat16, "k")
+    Lk = k.shape[1]
+    _need(k, torch.bfloat16, "k", (B, Lk, H, D))
+    _need(v, torch.bfloat16, "v", (B, Lk, H, D))
+    if table is not None:
+        _need(table, torch.float32, "table")
+    o = torch.empty_like(q) if out is None else out
+    _need(o, torch.bfloat16, "out", q.shape)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(lse, torch.float32, "lse", (B, H, Lq))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = partial_fwd_workspace_bytes(B, Lk, H, D, table is not None)
+    ws = _workspace(nbytes, q.device, workspace)
+    g = _grid(grid if grid is not None else (1, 1, max(q_offset + Lq, k_offset + Lk)))
+    _check(lib().wanattn_partial_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Lq, Lk, H, D, g, _rope(rope),
+                                     _ptr(table), int(q_offset), int(k_offset), scale, _ptr(ws),
+                                     nbytes if ws is None else ws.numel(), _stream(q.device)))
+    return o, lse
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse=None, want_lse=True):
+    """Exact merge of partial (O_r, LSE_r) over disjoint key sets.  Returns (o, lse)."""
+    torch = _torch()
+    R = len(o_parts)
+    if R != len(lse_parts) or not 1 <= R <= 16:
+        raise ValueError("need 1..16 matching partial outputs and LSEs")
+    B, L, H, D = o_parts[0].shape
+    for t in o_parts:
+        _need(t, torch.bfloat16, "o_parts[r]", (B, L, H, D))
+    for t in lse_parts:
+        _need(t, torch.float32, "lse_parts[r]", (B, H, L))
+    o = torch.empty_like(o_parts[0]) if out is None else out
+    _need(o, torch.bfloat16, "out", (B, L, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=o.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (B, H, L))
+    optrs = (_vp * R)(*[t.data_ptr() for t in o_parts])
+    lptrs = (_vp * R)(*[t.data_ptr() for t in lse_parts])
+    _check(lib().wanattn_lse_merge(optrs, lptrs, R, _ptr(o), _ptr(lse), B, L, H, D, _stream(o.device)))
     return o, lse

@@ -78,22 +78,27 @@ WANATTN_API size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, 
   return self_fwd_ws_bytes(B, L, H, D, with_rope);
 }
 
-WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
-                                 int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
-                                 void* ws, size_t ws_bytes, void* stream) {
-  const int rc = validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes);
-  if (rc != WANATTN_OK) return rc;
-  const hipStream_t s = (hipStream_t)stream;
+namespace wanattn {
+namespace {
+
+// Self-attention forward over (possibly sharded or length-limited) tokens:
+// prep pass into the workspace, then the attention kernel.  lens: [B] valid
+// token counts (queries and keys) or nullptr; q_pos0 / k_pos0: RoPE token
+// index of the first query / key row.
+int run_self_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Lq, int Lk, int H,
+                 int D, wanattn_grid g, wanattn_rope r, const float* table, float scale, void* ws,
+                 const int32_t* lens, int q_pos0, int k_pos0, hipStream_t s) {
   const RopeDev rope = make_rope(g, r, table);
   // K (with RoPE rotated once, instead of on every query tile's visit, and
   // stored in fp16 with a power-of-two exponent per tile) and V are rewritten
   // in the forward's 64-key tile layout in one pass; queries are rotated on
   // load.
-  const FwdWsLayout wl = self_fwd_ws_layout(B, L, H, D, table != nullptr);
+  const FwdWsLayout wl = self_fwd_ws_layout(B, Lk, H, D, table != nullptr);
   uint16_t* kt = (uint16_t*)((uint8_t*)ws + wl.kt);
   uint16_t* vt = (uint16_t*)((uint8_t*)ws + wl.vt);
   int* kexp = table != nullptr ? (int*)((uint8_t*)ws + wl.kexp) : nullptr;
-  const int e = hip_status(launch_kv_tiles((const uint16_t*)k, (const uint16_t*)v, kt, kexp, vt, B, L, H, rope, s));
+  const int e = hip_status(
+      launch_kv_tiles((const uint16_t*)k, (const uint16_t*)v, kt, kexp, vt, B, Lk, H, rope, lens, k_pos0, s));
   if (e != WANATTN_OK) return e;
   FwdParams p{};
   p.q = (const uint16_t*)q;
@@ -101,17 +106,73 @@ WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, vo
   p.v = (const uint16_t*)v;
   p.o = (uint16_t*)o;
   p.lse = lse;
-  p.k_lens = nullptr;
+  p.k_lens = lens;
+  p.q_lens = lens;
+  p.q_pos0 = q_pos0;
+  p.k_pos0 = k_pos0;
   p.kt = kt;
   p.kexp = kexp;
   p.vt = vt;
   p.rope = rope;
   p.B = B;
-  p.Lq = L;
-  p.Lk = L;
+  p.Lq = Lq;
+  p.Lk = Lk;
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
   return hip_status(launch_attn_fwd(p, s));
+}
+
+}  // namespace
+}  // namespace wanattn
+
+WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
+                                 int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  const int rc = validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, nullptr, 0, 0, (hipStream_t)stream);
+}
+
+WANATTN_API int wanattn_self_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int32_t* seq_lens, int B, int L, int H, int D, wanattn_grid g,
+                                        wanattn_rope r, const float* table, float scale, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  const int rc = validate_self_fwd_varlen(q, k, v, o, lse, seq_lens, B, L, H, D, g, r, table, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, seq_lens, 0, 0, (hipStream_t)stream);
+}
+
+WANATTN_API size_t wanattn_partial_fwd_workspace_bytes(int B, int Lk, int H, int D, int with_rope) {
+  return self_fwd_ws_bytes(B, Lk, H, D, with_rope);
+}
+
+WANATTN_API int wanattn_partial_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Lq,
+                                    int Lk, int H, int D, wanattn_grid g, wanattn_rope r, const float* table,
+                                    int q_offset, int k_offset, float scale, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  const int rc =
+      validate_partial_fwd(q, k, v, o, lse, B, Lq, Lk, H, D, g, r, table, q_offset, k_offset, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  return run_self_fwd(q, k, v, o, lse, B, Lq, Lk, H, D, g, r, table, scale, ws, nullptr, q_offset, k_offset,
+                      (hipStream_t)stream);
+}
+
+WANATTN_API int wanattn_lse_merge(const void* const* o_parts, const float* const* lse_parts, int R, void* o,
+                                  float* lse, int B, int L, int H, int D, void* stream) {
+  const int rc = validate_lse_merge(o_parts, lse_parts, R, o, lse, B, L, H, D);
+  if (rc != WANATTN_OK) return rc;
+  MergeParams p{};
+  for (int i = 0; i < R; ++i) {
+    p.o[i] = (const uint16_t*)o_parts[i];
+    p.lse[i] = lse_parts[i];
+  }
+  p.out = (uint16_t*)o;
+  p.out_lse = lse;
+  p.R = R;
+  p.B = B;
+  p.L = L;
+  p.H = H;
+  return hip_status(launch_lse_merge(p, (hipStream_t)stream));
 }
 
 WANATTN_API size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope) {

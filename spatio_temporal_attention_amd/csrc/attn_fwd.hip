@@ -78,12 +78,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
 
   // ---- query fragments (B operand of S^T = K Q^T): lane holds row i, d in [16s + 8*half, +8)
   const int i = qt * FWD_BR + wave * 32 + col;
-  const bool row_ok = i < p.Lq;
+  int n_q = p.Lq;
+  if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
+  const bool row_ok = i < n_q;
   bf16x8 qf[8];       // F16: fp16 bit patterns
   float g_q = p.scale_log2;   // score factor of this wave: s * log2(e) = g_q * 2^e_t * S
   {
     TokenPos pos{0, 0, 0};
-    if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, i);
+    if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, p.q_pos0 + i);
     if (F16) {
       float y[8][8];   // rotated query, fp32
       float mq = 0.f;
@@ -339,7 +341,7 @@ hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   // and their exponents (self-attention only).
   const bool f16 = p.rope.table != nullptr;
   const bool vt = p.kt != nullptr;
-  if (vt && (p.vt == nullptr || p.k_lens != nullptr || p.Lk != p.Lq)) return hipErrorInvalidValue;
+  if (vt && p.vt == nullptr) return hipErrorInvalidValue;
   // The tiles of one (b, h) are addressed through a buffer resource of 32-bit extent.
   if (vt && (int64_t)((p.Lk + FWD_BC - 1) / FWD_BC) * (TILE_ELEMS * 2) > (int64_t)0xffffffff)
     return hipErrorInvalidValue;

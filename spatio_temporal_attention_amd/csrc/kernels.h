@@ -16,6 +16,8 @@ struct FwdParams {
   uint16_t* o;
   float* lse;               // [B, H, Lq] or nullptr
   const int32_t* k_lens;    // [B] valid key counts or nullptr (all Lk)
+  const int32_t* q_lens;    // [B] valid query counts or nullptr (all Lq); rows past it are not written
+  int q_pos0, k_pos0;       // RoPE token index of query row 0 and key row 0 (shards of a longer sequence)
   // Self-attention: k and v in the tile layout of launch_kv_tiles (then k/v
   // above are unused), [B, H, ceil(Lk/64)] tiles; nullptr: read k/v directly.
   const uint16_t* kt;       // keys, tiles of [64][128]: bf16, or with RoPE fp16 of R(p) k * 2^-e_t
@@ -55,8 +57,20 @@ hipError_t launch_rope_table(float* table, int f, int h, int w, int d_f, int d_h
                              hipStream_t stream);
 hipError_t launch_rope3d(const uint16_t* x, uint16_t* y, int B, int L, int H, const RopeDev& rope,
                          bool inverse, hipStream_t stream);
+// lens: [B] valid token counts (tokens past them are treated as zero) or nullptr;
+// pos0: RoPE token index of row 0.
 hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, int* kexp, uint16_t* vt, int B, int L,
-                           int H, const RopeDev& rope, hipStream_t stream);
+                           int H, const RopeDev& rope, const int32_t* lens, int pos0, hipStream_t stream);
+// O = sum_r exp(LSE_r - LSE) O_r, LSE = ln sum_r exp(LSE_r) over R <= MERGE_MAX partial results.
+constexpr int MERGE_MAX = 16;
+struct MergeParams {
+  const uint16_t* o[MERGE_MAX];   // [B, L, H, 128] bf16
+  const float* lse[MERGE_MAX];    // [B, H, L]
+  uint16_t* out;
+  float* out_lse;                 // or nullptr
+  int R, B, L, H;
+};
+hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
                               uint16_t* vr, int B, int L, int H, const RopeDev& rope, hipStream_t stream);

@@ -38,22 +38,23 @@ __device__ __forceinline__ int frag_chunk(int tid) { return tid & 15; }
 
 // Load tokens [64*tile, +64) of head (b, h) of a [B, L, H, 128] bf16 tensor,
 // optionally rotated (fp32), and return this thread's max |x|.
+// Tokens at or past `valid` (<= L) are zero; `pos0` is the RoPE token index of row 0.
 __device__ __forceinline__ float load_tile(TileFrag& f, const uint16_t* __restrict__ x, int b, int h, int tile, int L,
-                                           int H, const RopeDev* rope, int tid) {
+                                           int H, const RopeDev* rope, int tid, int valid, int pos0) {
   float m = 0.f;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int n = tile * TILE_ROWS + frag_token(tid, it);
     const int ch = frag_chunk(tid);
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (n < L) v = *reinterpret_cast<const u32x4*>(x + (((int64_t)b * L + n) * H + h) * HD + ch * 8);
+    if (n < valid) v = *reinterpret_cast<const u32x4*>(x + (((int64_t)b * L + n) * H + h) * HD + ch * 8);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f.x[it][2 * t] = bf16_lo(v[t]);
       f.x[it][2 * t + 1] = bf16_hi(v[t]);
     }
-    if (rope != nullptr && n < L) {
-      const TokenPos pos = token_pos(*rope, n);
+    if (rope != nullptr && n < valid) {
+      const TokenPos pos = token_pos(*rope, pos0 + n);
 #pragma unroll
       for (int t = 0; t < 4; ++t) rope_rotate(f.x[it][2 * t], f.x[it][2 * t + 1], rope_cs(*rope, pos, 4 * ch + t), false);
     }
@@ -128,7 +129,7 @@ template <bool F16>
 __global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                        uint16_t* __restrict__ kt, int* __restrict__ kexp,
                                                        uint16_t* __restrict__ vt, int L, int H, int nt,
-                                                       RopeDev rope) {
+                                                       RopeDev rope, const int32_t* __restrict__ lens, int pos0) {
   __shared__ __attribute__((aligned(16))) StageRows s;
   __shared__ float wmax[4];
   const int tile = blockIdx.x % nt;
@@ -137,8 +138,9 @@ __global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restric
   const int b = bh / H;
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
+  const int valid = lens != nullptr ? min(max(lens[b], 0), L) : L;
   TileFrag f;
-  const float mk = load_tile(f, k, b, h, tile, L, H, F16 ? &rope : nullptr, tid);
+  const float mk = load_tile(f, k, b, h, tile, L, H, F16 ? &rope : nullptr, tid, valid, pos0);
   if (F16) {
     const int e = pow2_exponent_15(block_max(mk, wmax, tid));
     if (tid == 0) kexp[blockIdx.x] = e;
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restric
   } else {
     store_row_tile_bf16(kt + off, f, tid);
   }
-  load_tile(f, v, b, h, tile, L, H, nullptr, tid);
+  load_tile(f, v, b, h, tile, L, H, nullptr, tid, valid, 0);
   stage_bf16(s, f, tid);
   __syncthreads();
   store_t_tile(vt + off, s, tid);
@@ -167,14 +169,14 @@ __global__ __launch_bounds__(256) void bwd_k_tiles_kernel(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
   TileFrag f;
-  const float mk = load_tile(f, k, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid);
+  const float mk = load_tile(f, k, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid, L, 0);
   const int e = pow2_exponent_15(block_max(mk, wmax, tid));
   if (tid == 0) kexp[blockIdx.x] = e;
   store_row_tile_f16(kf + off, f, e, tid);
   stage_bf16(s, f, tid);
   __syncthreads();
   store_t_tile(kt + off, s, tid);
-  load_tile(f, v, b, h, tile, L, H, nullptr, tid);
+  load_tile(f, v, b, h, tile, L, H, nullptr, tid, L, 0);
   store_row_tile_bf16(vr + off, f, tid);
 }
 
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
   TileFrag f;
-  const float mq = load_tile(f, q, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid);
+  const float mq = load_tile(f, q, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid, L, 0);
   const int e = pow2_exponent_15(block_max(mq, wmax, tid));
   if (tid == 0) qexp[blockIdx.x] = e;
   store_row_tile_f16(qf + off, f, e, tid);
@@ -205,11 +207,11 @@ __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __rest
   __syncthreads();   // the staging rows are reused below
 
   // dO: row tile, T tile, and Delta = <dO, O> per token (16 lanes per row).
-  load_tile(f, dout, b, h, tile, L, H, nullptr, tid);
+  load_tile(f, dout, b, h, tile, L, H, nullptr, tid, L, 0);
   store_row_tile_bf16(dor + off, f, tid);
   stage_bf16(s, f, tid);
   TileFrag g;
-  load_tile(g, o, b, h, tile, L, H, nullptr, tid);
+  load_tile(g, o, b, h, tile, L, H, nullptr, tid, L, 0);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     float d = 0.f;
@@ -237,16 +239,18 @@ hipError_t grid_of_tiles(int B, int L, int H, int& nt, dim3& grid) {
 }  // namespace
 
 hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, int* kexp, uint16_t* vt, int B, int L,
-                           int H, const RopeDev& rope, hipStream_t stream) {
+                           int H, const RopeDev& rope, const int32_t* lens, int pos0, hipStream_t stream) {
   int nt;
   dim3 grid;
   if (grid_of_tiles(B, L, H, nt, grid) != hipSuccess) return hipErrorInvalidValue;
   const bool f16 = rope.table != nullptr;
   if (f16 != (kexp != nullptr)) return hipErrorInvalidValue;
   if (f16)
-    hipLaunchKernelGGL(kv_tiles_kernel<true>, grid, dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt, rope);
+    hipLaunchKernelGGL(kv_tiles_kernel<true>, grid, dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt, rope, lens,
+                       pos0);
   else
-    hipLaunchKernelGGL(kv_tiles_kernel<false>, grid, dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt, rope);
+    hipLaunchKernelGGL(kv_tiles_kernel<false>, grid, dim3(256), 0, stream, k, v, kt, kexp, vt, L, H, nt, rope, lens,
+                       pos0);
   return hipGetLastError();
 }
 

@@ -125,6 +125,51 @@ int validate_self_fwd(const void* q, const void* k, const void* v, const void* o
   return WANATTN_OK;
 }
 
+int validate_self_fwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const int32_t* seq_lens, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
+                             const float* table, float scale, const void* ws, size_t ws_bytes) {
+  if (seq_lens == nullptr) return WANATTN_ERR_NULL;
+  WANATTN_TRY(validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes));
+  return aligned(seq_lens, 4) ? WANATTN_OK : WANATTN_ERR_ALIGN;
+}
+
+int validate_partial_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Lq,
+                         int Lk, int H, int D, wanattn_grid g, wanattn_rope r, const float* table, int q_offset,
+                         int k_offset, float scale, const void* ws, size_t ws_bytes) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return WANATTN_ERR_NULL;
+  WANATTN_TRY(check_dims(B, Lq, H, D));
+  WANATTN_TRY(check_dims(B, Lk, H, D));
+  if (q_offset < 0 || k_offset < 0) return WANATTN_ERR_SHAPE;
+  if (table != nullptr) {
+    WANATTN_TRY(check_rope_only(g, r, D));
+    const int64_t total = (int64_t)g.f * g.h * g.w;
+    if ((int64_t)q_offset + Lq > total || (int64_t)k_offset + Lk > total) return WANATTN_ERR_SHAPE;
+    if (!aligned(table, 16)) return WANATTN_ERR_ALIGN;
+  }
+  WANATTN_TRY(check_scale(scale));
+  const void* bufs[] = {q, k, v, o};
+  for (const void* p : bufs) WANATTN_TRY(check_bf16(p));
+  if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < self_fwd_ws_bytes(B, Lk, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
+int validate_lse_merge(const void* const* o_parts, const float* const* lse_parts, int R, const void* o,
+                       const float* lse, int B, int L, int H, int D) {
+  if (o_parts == nullptr || lse_parts == nullptr || o == nullptr) return WANATTN_ERR_NULL;
+  if (R < 1 || R > 16) return WANATTN_ERR_SHAPE;
+  WANATTN_TRY(check_dims(B, L, H, D));
+  for (int r = 0; r < R; ++r) {
+    if (o_parts[r] == nullptr || lse_parts[r] == nullptr) return WANATTN_ERR_NULL;
+    WANATTN_TRY(check_bf16(o_parts[r]));
+    if (!aligned(lse_parts[r], 4)) return WANATTN_ERR_ALIGN;
+  }
+  WANATTN_TRY(check_bf16(o));
+  if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
 int validate_self_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, const void* dq, const void* dk, const void* dv, int B, int L, int H,
                       int D, wanattn_grid g, wanattn_rope r, const float* table, float scale, const void* ws,

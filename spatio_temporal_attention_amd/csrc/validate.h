@@ -47,6 +47,14 @@ int validate_self_bwd(const void* q, const void* k, const void* v, const void* o
                       const void* dout, const void* dq, const void* dk, const void* dv, int B, int L, int H,
                       int D, wanattn_grid g, wanattn_rope r, const float* table, float scale, const void* ws,
                       size_t ws_bytes);
+int validate_self_fwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const int32_t* seq_lens, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
+                             const float* table, float scale, const void* ws, size_t ws_bytes);
+int validate_partial_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Lq,
+                         int Lk, int H, int D, wanattn_grid g, wanattn_rope r, const float* table, int q_offset,
+                         int k_offset, float scale, const void* ws, size_t ws_bytes);
+int validate_lse_merge(const void* const* o_parts, const float* const* lse_parts, int R, const void* o,
+                       const float* lse, int B, int L, int H, int D);
 int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
                        const float* lse, int B, int Lq, int Lk, int H, int D, float scale);
 

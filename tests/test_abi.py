@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libwanattn.so"
         assert n in wa._SIGNATURES, f"{n} has no binding"
@@ -159,3 +159,50 @@ def test_binding_token_grid_matches_golden():
         assert list(wa.token_grid(c["frames"], c["height"], c["width"])) == c["grid"]
     with pytest.raises(ValueError):
         wa.token_grid(80, 480, 832)
+
+
+def test_varlen_partial_merge_validation(lib):
+    """Every call below has at least one invalid argument, so nothing is launched."""
+    import ctypes
+    lens_ok = P
+    def varlen(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, lens=lens_ok, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P,
+                 scale=0.088, ws=P, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.wanattn_self_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["lens"], a["B"], a["L"], a["H"],
+                                           a["D"], a["g"], a["r"], a["table"], a["scale"], a["ws"], a["ws_bytes"], None)
+    assert varlen(lens=None) == NULL
+    assert varlen(lens=P + 2) == ALIGN
+    assert varlen(L=321) == SHAPE
+    assert varlen(ws=None) == WS
+
+    def partial(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Lq=100, Lk=64, H=2, D=128, g=GRID, r=ROPE, table=P, qo=0, ko=0,
+                 scale=0.088, ws=P, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.wanattn_partial_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"], a["H"],
+                                       a["D"], a["g"], a["r"], a["table"], a["qo"], a["ko"], a["scale"], a["ws"],
+                                       a["ws_bytes"], None)
+    assert partial(qo=-1) == SHAPE
+    assert partial(qo=221) == SHAPE                  # 221 + 100 > 320 grid tokens
+    assert partial(ko=257) == SHAPE
+    assert partial(Lk=0) == SHAPE
+    assert partial(table=ODD) == ALIGN
+    assert partial(ws_bytes=lib.wanattn_partial_fwd_workspace_bytes(1, 64, 2, 128, 1) - 1) == WS
+    assert partial(v=None) == NULL
+    assert lib.wanattn_partial_fwd_workspace_bytes(1, 64, 2, 128, 1) == lib.wanattn_self_fwd_workspace_bytes(
+        1, 64, 2, 128, 1)
+
+    def merge(R=2, parts=None, lparts=None, o=P, lse=P, B=1, L=70, H=2):
+        arr = ctypes.c_void_p * max(R, 1)
+        op = arr(*(parts if parts is not None else [P] * max(R, 1)))
+        lp = arr(*(lparts if lparts is not None else [P] * max(R, 1)))
+        return lib.wanattn_lse_merge(op, lp, R, o, lse, B, L, H, 128, None)
+    assert merge(R=0) == SHAPE
+    assert merge(R=17) == SHAPE
+    assert merge(parts=[P, None]) == NULL
+    assert merge(lparts=[P, P + 2]) == ALIGN
+    assert merge(parts=[P, ODD]) == ALIGN
+    assert merge(o=None) == NULL
+    assert merge(L=0) == SHAPE
+

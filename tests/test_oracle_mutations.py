@@ -8,6 +8,7 @@ import oracle.reference as ref
 import test_oracle_attention as fwd_pins
 import test_oracle_backward as bwd_pins
 import test_oracle_rope as rope_pins
+import test_oracle_shards as shard_pins
 
 
 def _rope_apply_wrong_sign(x, angles, inverse=False):
@@ -51,6 +52,18 @@ def _attention_no_scale(qt, kt, v, scale):
     return _ORIG_ATTN(qt, kt, v, 1.0 if scale != 0 else 0.0)
 
 
+def _partial_local_positions(q, k, v, scale, q_offset, k_offset, grid=None, rope=None, rows=None):
+    return _ORIG_PARTIAL(q, k, v, scale, 0, 0, grid, rope, rows)
+
+
+def _merge_unnormalized(o_parts, lse_parts):
+    lse_st = np.stack(lse_parts)
+    m = lse_st.max(axis=0)
+    o = sum(np.asarray(op) * np.transpose(np.exp(l - m), (0, 2, 1))[..., None] for op, l in zip(o_parts, lse_parts))
+    return o, m + np.log(np.exp(lse_st - m).sum(axis=0))
+
+
+_ORIG_PARTIAL = ref.partial_fwd_ref
 _ORIG_APPLY = ref.rope_apply
 _ORIG_POS = ref.positions
 _ORIG_ROTATED = ref._rotated
@@ -71,6 +84,10 @@ MUTATIONS = [
      [lambda: bwd_pins.test_self_bwd_finite_differences(ref.RopeSpec(4, 6, 6, 10000.0), 16, (2, 2, 3))]),
     ("dropped softmax scale", "attention_rows_ref", _attention_no_scale,
      [fwd_pins.test_self_fwd_matches_torch_sdpa_without_rope]),
+    ("shard positions taken as local indices", "partial_fwd_ref", _partial_local_positions,
+     [shard_pins.test_query_shard_rows_match_brute_force, shard_pins.test_merge_of_key_shards_is_full_attention]),
+    ("merge weights not normalized by the total LSE", "lse_merge_ref", _merge_unnormalized,
+     [shard_pins.test_merge_of_key_shards_is_full_attention, shard_pins.test_merge_closed_forms]),
 ]
 
 
