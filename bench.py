@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the varlen / ring-shard / merge measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain device copy of known size (for scaling HBM counters)")
     return ap.parse_args()
@@ -86,6 +87,77 @@ def cpu_baseline(inp, w, rope, scale):
             "sample": f"self-attention forward (fp64 NumPy, 3D RoPE) of {rows.shape[2]} seeded query rows "
                       f"x {w.H} heads against all {w.L} keys of the 720p workload; {dt:.2f} s",
             "seconds": dt, "flop": flop}
+
+
+def _time(fn, reps=3):
+    """Mean ms of `fn` over `reps` calls after one warm call (HIP events on the current stream)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def bench_next_rows(wa, torch, synth, dev, rope):
+    """The rows beyond the step, each on its own realistic shape (timed after the step, not in it):
+    - one Ring hop of Ulysses-8 x Ring-2 context parallelism at 256K tokens (grid 64x64x64): a
+      131,072-token query shard x a 131,072-token key/value shard, 5 heads, global RoPE positions,
+      then the exact merge of the two hops' partial results;
+    - the text cross-attention backward at the step's shape;
+    - a joint video + image batch: a 720p clip (75,600 tokens) and one image frame (3,600 tokens)
+      padded to 75,600, 40 heads, variable-length self-attention."""
+    out = {}
+    grid = (64, 64, 64)
+    Lh, H = 131072, 5
+    g = torch.Generator(device=dev).manual_seed(7)
+    q, k, v = (torch.randn((1, Lh, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    table = wa.rope_table(grid, rope, device=dev)
+    ws = torch.empty(wa.partial_fwd_workspace_bytes(1, Lh, H), dtype=torch.uint8, device=dev)
+    o1, l1 = torch.empty_like(q), torch.empty((1, H, Lh), dtype=torch.float32, device=dev)
+    o2, l2 = torch.empty_like(q), torch.empty((1, H, Lh), dtype=torch.float32, device=dev)
+    ms = _time(lambda: wa.partial_fwd(q, k, v, Lh, 0, grid=grid, table=table, rope=rope, out=o1, lse=l1,
+                                      workspace=ws))
+    wa.partial_fwd(q, k, v, Lh, Lh, grid=grid, table=table, rope=rope, out=o2, lse=l2, workspace=ws)
+    flop = 4.0 * H * Lh * Lh * 128
+    out["partial_fwd"] = {"workload": "ring hop at 256K tokens: q tokens [131072, 262144) x k/v tokens [0, 131072), "
+                                      "5 heads, grid 64x64x64, RoPE at global positions",
+                          "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    om, lm = torch.empty_like(q), torch.empty((1, H, Lh), dtype=torch.float32, device=dev)
+    ms = _time(lambda: wa.lse_merge([o1, o2], [l1, l2], out=om, lse=lm), reps=10)
+    nbytes = 3.0 * q.numel() * 2 + 3.0 * l1.numel() * 4
+    out["lse_merge"] = {"workload": "2 partials [1, 131072, 5, 128] bf16 + LSE", "ms": round(ms, 4),
+                        "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del q, k, v, o1, o2, om, ws
+    # text cross-attention backward at the step's shape: 75,600 video tokens over 512 text tokens (336 valid)
+    L, H, Lt = 75600, 40, 512
+    q, do = (torch.randn((1, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    tk, tv = (torch.randn((1, Lt, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    kl = torch.tensor([336], dtype=torch.int32, device=dev)
+    o, lse = wa.cross_fwd(q, tk, tv, kl)
+    ws = torch.empty(wa.cross_bwd_workspace_bytes(1, L, Lt, H), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(tk), torch.empty_like(tv)
+    ms = _time(lambda: wa.cross_bwd(q, tk, tv, kl, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv))
+    flop = 8.0 * H * L * 336 * 128
+    out["cross_bwd"] = {"workload": "720p video tokens (75,600) over 512 text tokens (336 valid), 40 heads",
+                        "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    del q, do, tk, tv, o, ws, dq, dk, dv
+    L, H = 75600, 40
+    q, k, v = (torch.randn((2, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    lens = torch.tensor([L, 3600], dtype=torch.int32, device=dev)
+    table = wa.rope_table((21, 45, 80), rope, device=dev)
+    ws = torch.empty(wa.self_fwd_workspace_bytes(2, L, H), dtype=torch.uint8, device=dev)
+    o, lse = torch.empty_like(q), torch.empty((2, H, L), dtype=torch.float32, device=dev)
+    ms = _time(lambda: wa.self_fwd_varlen(q, k, v, lens, grid=(21, 45, 80), table=table, rope=rope, out=o, lse=lse,
+                                          workspace=ws), reps=2)
+    flop = 4.0 * H * 128 * (L * L + 3600 * 3600)
+    out["varlen_fwd"] = {"workload": "720p clip (75,600 tokens) + 1-frame image (3,600) padded to 75,600, 40 heads",
+                         "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    return out
 
 
 def main():
@@ -226,6 +298,8 @@ def main():
                      "flop_per_launch": fwd_flop},
     }
     result.update(extra)
+    if not args.fwd_only and not args.no_extras:
+        result["next_rows"] = bench_next_rows(wa, torch, synth, dev, rope)
     if not args.no_cpu_baseline:
         log("running the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(inp, w, rope, scale)

@@ -225,6 +225,30 @@ int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t
                       void* o, float* lse,
                       int B, int Lq, int Lk, int H, int D, float scale, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Cross-attention backward (training back-propagates through the text
+ * cross-attention of every block: [lit619] Key takeaways, Backbone; [notes]
+ * 3. Training).  The calculus of wanattn_cross_fwd, given its o and lse
+ * (lse required) and the output gradient dout:
+ *   P_ij = exp(scale <q_i, k_j> - LSE_i) for valid keys j < k_lens[b], else 0;
+ *   Delta_i = <dout_i, o_i>;  dV_j = sum_i P_ij dout_i;
+ *   dS_ij = P_ij (<dout_i, v_j> - Delta_i);
+ *   dq_i = scale sum_j dS_ij k_j;  dk_j = scale sum_i dS_ij q_i.
+ * Padded keys (j >= k_lens[b]) get dk = dv = 0 and are never read; rows with
+ * no valid key (LSE = -inf) get dq = 0.  dq: [B, Lq, H, D]; dk, dv: [B, Lk,
+ * H, D] bf16.  k_lens: device int32 [B] (clamped to [0, Lk]) or NULL (all
+ * valid).  The score product runs in fp16 on power-of-two-scaled 64-token
+ * tiles, as in the self-attention backward.
+ * Workspace (required, 16-byte aligned): wanattn_cross_bwd_workspace_bytes.
+ * ------------------------------------------------------------------------- */
+size_t wanattn_cross_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int D);
+
+int wanattn_cross_bwd(const void* q, const void* k, const void* v, const int32_t* k_lens,
+                      const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv,
+                      int B, int Lq, int Lk, int H, int D, float scale,
+                      void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -73,6 +73,9 @@ _SIGNATURES = {
     "wanattn_partial_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, Grid, Rope, _vp, _i, _i, _f, _vp, _sz,
                                  _vp]),
     "wanattn_lse_merge": (_i, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wanattn_cross_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "wanattn_cross_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz,
+                               _vp]),
 }
 
 _LIB = None
@@ -352,3 +355,37 @@ def lse_merge(o_parts, lse_parts, out=None, lse=None, want_lse=True):
     lptrs = (_vp * R)(*[t.data_ptr() for t in lse_parts])
     _check(lib().wanattn_lse_merge(optrs, lptrs, R, _ptr(o), _ptr(lse), B, L, H, D, _stream(o.device)))
     return o, lse
+
+
+def cross_bwd_workspace_bytes(B, Lq, Lk, H, D=HEAD_DIM) -> int:
+    return int(lib().wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D))
+
+
+def cross_bwd(q, k, v, k_lens, o, lse, dout, scale=None, workspace=None, dq=None, dk=None, dv=None):
+    """Cross-attention backward (key padding by k_lens).  Returns (dq, dk, dv)."""
+    torch = _torch()
+    _need(q, torch.bfloat16, "q")
+    B, Lq, H, D = q.shape
+    _need(k, torch.bfloat16, "k")
+    Lk = k.shape[1]
+    _need(k, torch.bfloat16, "k", (B, Lk, H, D))
+    _need(v, torch.bfloat16, "v", (B, Lk, H, D))
+    if k_lens is not None:
+        _need(k_lens, torch.int32, "k_lens", (B,))
+    _need(o, torch.bfloat16, "o", q.shape)
+    _need(dout, torch.bfloat16, "dout", q.shape)
+    _need(lse, torch.float32, "lse", (B, H, Lq))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, torch.bfloat16, "dq", q.shape)
+    _need(dk, torch.bfloat16, "dk", k.shape)
+    _need(dv, torch.bfloat16, "dv", v.shape)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = cross_bwd_workspace_bytes(B, Lq, Lk, H, D)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib().wanattn_cross_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(k_lens), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), B, Lq, Lk, H, D, scale, _ptr(ws),
+                                   nbytes if ws is None else ws.numel(), _stream(q.device)))
+    return dq, dk, dv
+

@@ -179,17 +179,17 @@ WANATTN_API size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, 
   return self_bwd_ws_bytes(B, L, H, D, with_rope);
 }
 
-WANATTN_API int wanattn_self_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                                 const void* dout, void* dq, void* dk, void* dv, int B, int L, int H, int D,
-                                 wanattn_grid g, wanattn_rope r, const float* table, float scale, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  const int rc = validate_self_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, L, H, D, g, r, table, scale, ws, ws_bytes);
-  if (rc != WANATTN_OK) return rc;
-  const hipStream_t s = (hipStream_t)stream;
-  // Prep passes: Q and K (rotated with a table) as fp16 tiles with the
-  // forward's power-of-two exponents, their bf16 transposes, dO and V tiles,
-  // and Delta; then the dK/dV and dQ passes over those tiles.
-  const BwdWsLayout w = self_bwd_ws_layout(B, L, H, D);
+namespace wanattn {
+namespace {
+
+// Backward over q-side [B, Lq, H, D] and k-side [B, Lk, H, D] tensors: prep
+// passes (Q and K, rotated with a table, as fp16 tiles with the forward's
+// power-of-two exponents, their bf16 transposes, dO and V tiles, Delta), then
+// the dK/dV and dQ passes over those tiles.  k_lens: key padding or nullptr.
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+            void* dk, void* dv, const int32_t* k_lens, int B, int Lq, int Lk, int H, int D, const RopeDev& rope,
+            float scale, void* ws, hipStream_t s) {
+  const BwdWsLayout w = bwd_ws_layout(B, Lq, Lk, H, D);
   uint8_t* base = (uint8_t*)ws;
   BwdParams p{};
   p.qf = (const uint16_t*)(base + w.qf);
@@ -206,24 +206,53 @@ WANATTN_API int wanattn_self_bwd(const void* q, const void* k, const void* v, co
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
-  p.rope = make_rope(g, r, table);
+  p.k_lens = k_lens;
+  p.rope = rope;
   p.B = B;
-  p.L = L;
+  p.Lq = Lq;
+  p.Lk = Lk;
   p.H = H;
   p.scale = scale;
   p.scale_log2 = scale * LOG2E_F;
   int e = hip_status(launch_bwd_k_tiles((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)(base + w.kf),
                                         (int*)(base + w.kexp), (uint16_t*)(base + w.kt), (uint16_t*)(base + w.vr), B,
-                                        L, H, p.rope, s));
+                                        Lk, H, rope, k_lens, s));
   if (e != WANATTN_OK) return e;
   e = hip_status(launch_bwd_q_tiles((const uint16_t*)q, (const uint16_t*)dout, (const uint16_t*)o,
                                     (uint16_t*)(base + w.qf), (int*)(base + w.qexp), (uint16_t*)(base + w.qt),
                                     (uint16_t*)(base + w.dor), (uint16_t*)(base + w.dot), (float*)(base + w.delta), B,
-                                    L, H, p.rope, s));
+                                    Lq, H, rope, s));
   if (e != WANATTN_OK) return e;
   e = hip_status(launch_bwd_dkdv(p, s));
   if (e != WANATTN_OK) return e;
   return hip_status(launch_bwd_dq(p, s));
+}
+
+}  // namespace
+}  // namespace wanattn
+
+WANATTN_API int wanattn_self_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, int B, int L, int H, int D,
+                                 wanattn_grid g, wanattn_rope r, const float* table, float scale, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  const int rc = validate_self_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, L, H, D, g, r, table, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, L, L, H, D, make_rope(g, r, table), scale, ws,
+                 (hipStream_t)stream);
+}
+
+WANATTN_API size_t wanattn_cross_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int D) {
+  return cross_bwd_ws_bytes(B, Lq, Lk, H, D);
+}
+
+WANATTN_API int wanattn_cross_bwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int Lq,
+                                  int Lk, int H, int D, float scale, void* ws, size_t ws_bytes, void* stream) {
+  const int rc =
+      validate_cross_bwd(q, k, v, k_lens, o, lse, dout, dq, dk, dv, B, Lq, Lk, H, D, scale, ws, ws_bytes);
+  if (rc != WANATTN_OK) return rc;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, k_lens, B, Lq, Lk, H, D, make_rope({1, 1, 1}, {0, 0, 0, 1.f}, nullptr),
+                 scale, ws, (hipStream_t)stream);
 }
 
 WANATTN_API int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, void* o,

@@ -67,6 +67,8 @@ __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* t
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup owns 128 keys (key tiles 2kb, 2kb+1); loop over 64-query tiles.
 // ---------------------------------------------------------------------------
+// KMASK: keys j >= k_lens[b] get P = 0 (cross-attention key padding).
+template <bool KMASK>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE_ELEMS];   // [buf][Q fp16 | (Rq)^T | dO | dO^T]
   __shared__ float lse2_s[2][TILE_ROWS];                                      // LSE * log2 e (+inf: no row)
@@ -84,18 +86,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int bh = logical / p.n_tiles;
   const int h = bh % p.H;
   const int b = bh / p.H;
-  const int nt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
+  const int nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;     // query tiles
+  const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;    // key tiles
   const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
+  const int64_t ktile0 = (int64_t)(b * p.H + h) * ntk;
 
   // This lane's key j: row 32*(wave%2) + col of key tile 2kb + wave/2.
   const int ktile = 2 * kb + (wv >> 1);
   const int j = kb * 128 + wave * 32 + col;
-  const bool key_ok = j < p.L;
-  const bool tile_ok = ktile < nt;
+  const bool key_ok = j < p.Lk;
+  const bool key_live = !KMASK || j < min(max(p.k_lens[b], 0), p.Lk);
+  const bool tile_ok = ktile < ntk;
   bf16x8 kf[8], vf[8];   // K fp16 (bit patterns), V bf16: B operands of S and dP
-  load_row_frags(kf, p.kf + (tile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
-  load_row_frags(vf, p.vr + (tile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
-  const int e_k = tile_ok ? p.kexp[tile0 + ktile] : 0;
+  load_row_frags(kf, p.kf + (ktile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
+  load_row_frags(vf, p.vr + (ktile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
+  const int e_k = tile_ok ? p.kexp[ktile0 + ktile] : 0;
 
   f32x16 dk_acc[4], dv_acc[4];
 #pragma unroll
@@ -103,8 +108,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     dk_acc[d] = f32x16{};
     dv_acc[d] = f32x16{};
   }
-  const float* lse_row = p.lse + ((int64_t)b * p.H + h) * p.L;
-  const float* delta_row = p.delta + ((int64_t)b * p.H + h) * p.L;
+  const float* lse_row = p.lse + ((int64_t)b * p.H + h) * p.Lq;
+  const float* delta_row = p.delta + ((int64_t)b * p.H + h) * p.Lq;
 
   uint32_t roff[4], toff[4];
 #pragma unroll
@@ -129,11 +134,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       buf_dma16(dotr, toff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][3], wv, i));
     }
     if (tid < TILE_ROWS) {
+      // rows past Lq, and rows with no valid key (LSE = -inf), contribute nothing
       const int i = t * TILE_ROWS + tid;
-      lse2_s[buf][tid] = (i < p.L) ? lse_row[i] * LOG2E : INFINITY;
+      const float l = (i < p.Lq) ? lse_row[i] : -INFINITY;
+      lse2_s[buf][tid] = (l > -INFINITY) ? l * LOG2E : INFINITY;
     } else if (tid < 2 * TILE_ROWS) {
       const int i = t * TILE_ROWS + tid - TILE_ROWS;
-      delta_s[buf][tid - TILE_ROWS] = (i < p.L) ? delta_row[i] : 0.f;
+      delta_s[buf][tid - TILE_ROWS] = (i < p.Lq) ? delta_row[i] : 0.f;
     }
   };
 
@@ -171,7 +178,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int r = qb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);   // query row in the tile
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2_s[buf][r]));
+        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2_s[buf][r]));
+        if (KMASK && !key_live) pe = 0.f;
         pv[jj] = pe;
         dsv[jj] = pe * (dp_acc[jj] - delta_s[buf][r]);
       }
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr) pos = token_pos(p.rope, j);
     const int64_t rs = (int64_t)p.H * HD;
-    const int64_t head_off = ((int64_t)b * p.L * p.H + h) * HD;
+    const int64_t head_off = ((int64_t)b * p.Lk * p.H + h) * HD;
     uint16_t* dkrow = p.dk + head_off + (int64_t)j * rs;
     uint16_t* dvrow = p.dv + head_off + (int64_t)j * rs;
     RopeDev none = p.rope;
@@ -235,20 +243,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const int bh = logical / p.n_tiles;
   const int h = bh % p.H;
   const int b = bh / p.H;
-  const int nt = (p.L + TILE_ROWS - 1) / TILE_ROWS;
+  const int nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;     // query tiles
+  const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;    // key tiles
   const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
+  const int64_t ktile0 = (int64_t)(b * p.H + h) * ntk;
+  const int n_keys = p.k_lens != nullptr ? min(max(p.k_lens[b], 0), p.Lk) : p.Lk;
+  const int nkt = (n_keys + TILE_ROWS - 1) / TILE_ROWS;  // key tiles visited
 
   // This lane's query i: row 32*(wave%2) + col of query tile 4qb + wave/2.
   const int qtile = 4 * qb + (wv >> 1);
   const int i = qb * 256 + wave * 32 + col;
-  const bool row_ok = i < p.L;
+  const bool row_ok = i < p.Lq;
   const bool tile_ok = qtile < nt;
   bf16x8 qf[8], dof[8];   // Q fp16 (bit patterns), dO bf16: B operands of S^T and dP^T
   load_row_frags(qf, p.qf + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
   load_row_frags(dof, p.dor + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
   const int e_q = tile_ok ? p.qexp[tile0 + qtile] : 0;
-  const int64_t stat = ((int64_t)b * p.H + h) * p.L + i;
-  const float lse2 = row_ok ? p.lse[stat] * LOG2E : INFINITY;
+  const int64_t stat = ((int64_t)b * p.H + h) * p.Lq + i;
+  const float lse_i = row_ok ? p.lse[stat] : -INFINITY;
+  const float lse2 = (lse_i > -INFINITY) ? lse_i * LOG2E : INFINITY;   // no valid key: P = 0
   const float delta = row_ok ? p.delta[stat] : 0.f;
 
   f32x16 dq_acc[4];
@@ -261,11 +274,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     roff[c] = rowtile_lane_off<DQ_WAVES>(wv, c, lane);
     toff[c] = ttile_lane_off<DQ_WAVES>(wv, c, lane);
   }
-  const uint32_t bytes = (uint32_t)nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
-  const __amdgpu_buffer_rsrc_t kfr = tile_rsrc(p.kf + tile0 * TILE_ELEMS, bytes);
-  const __amdgpu_buffer_rsrc_t ktr = tile_rsrc(p.kt + tile0 * TILE_ELEMS, bytes);
-  const __amdgpu_buffer_rsrc_t vrr = tile_rsrc(p.vr + tile0 * TILE_ELEMS, bytes);
-  const int* kexp = p.kexp + tile0;
+  const uint32_t bytes = (uint32_t)ntk * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+  const __amdgpu_buffer_rsrc_t kfr = tile_rsrc(p.kf + ktile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t ktr = tile_rsrc(p.kt + ktile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t vrr = tile_rsrc(p.vr + ktile0 * TILE_ELEMS, bytes);
+  const int* kexp = p.kexp + ktile0;
 
   auto stage = [&](int buf, int t) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
@@ -277,8 +290,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     }
   };
 
-  stage(0, 0);
-  int e_k = kexp[0];
+  int e_k = 0;
+  if (nkt > 0) {
+    stage(0, 0);
+    e_k = kexp[0];
+  }
   wait_vmem();
   __syncthreads();
 
@@ -304,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
         float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2));
         if (MASK) {
           const int key = t * TILE_ROWS + kb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
-          if (key >= p.L) pe = 0.f;
+          if (key >= n_keys) pe = 0.f;
         }
         dsv[jj] = pe * (dp_acc[jj] - delta);
       }
@@ -321,10 +337,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   };
 
   // Full tiles in the loop; a partial last tile is peeled off after it.
-  const int n_full = p.L / TILE_ROWS;
+  const int n_full = n_keys / TILE_ROWS;
   for (int t = 0; t < n_full; ++t) {
     const int buf = t & 1;
-    const bool has_next = t + 1 < nt;
+    const bool has_next = t + 1 < nkt;
     int e_k_next = 0;
     if (has_next) {
       stage(buf ^ 1, t + 1);
@@ -335,13 +351,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     e_k = e_k_next;
   }
-  if (n_full < nt) key_tile(std::true_type{}, n_full, n_full & 1);
+  if (n_full < nkt) key_tile(std::true_type{}, n_full, n_full & 1);
 
   if (row_ok) {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr) pos = token_pos(p.rope, i);
     const int64_t rs = (int64_t)p.H * HD;
-    uint16_t* dqrow = p.dq + ((int64_t)b * p.L * p.H + h) * HD + (int64_t)i * rs;
+    uint16_t* dqrow = p.dq + ((int64_t)b * p.Lq * p.H + h) * HD + (int64_t)i * rs;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -362,19 +378,22 @@ bool tiles_addressable(int L) {
 }  // namespace
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
-  if (!tiles_addressable(p.L)) return hipErrorInvalidValue;
+  if (!tiles_addressable(p.Lq) || !tiles_addressable(p.Lk)) return hipErrorInvalidValue;
   BwdParams q = p;
-  q.n_tiles = (p.L + 127) / 128;
+  q.n_tiles = (p.Lk + 127) / 128;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)total), dim3(64 * DKDV_WAVES), 0, stream, q);
+  if (p.k_lens != nullptr)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)total), dim3(64 * DKDV_WAVES), 0, stream, q);
+  else
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)total), dim3(64 * DKDV_WAVES), 0, stream, q);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
-  if (!tiles_addressable(p.L)) return hipErrorInvalidValue;
+  if (!tiles_addressable(p.Lq) || !tiles_addressable(p.Lk)) return hipErrorInvalidValue;
   BwdParams q = p;
-  q.n_tiles = (p.L + 255) / 256;
+  q.n_tiles = (p.Lq + 255) / 256;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)total), dim3(64 * DQ_WAVES), 0, stream, q);

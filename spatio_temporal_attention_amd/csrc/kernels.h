@@ -46,8 +46,9 @@ struct BwdParams {
   uint16_t* dq;             // [B, L, H, 128] bf16 outputs
   uint16_t* dk;
   uint16_t* dv;
+  const int32_t* k_lens;    // [B] valid key counts (keys past them get P = 0 and zero gradients) or nullptr
   RopeDev rope;             // rope.table != nullptr: rotate dq/dk back by minus the angle
-  int B, L, H;
+  int B, Lq, Lk, H;         // q-side tensors [B, Lq, H, 128], k-side [B, Lk, H, 128]
   float scale;
   float scale_log2;
   int n_tiles;              // set by the launchers
@@ -73,7 +74,8 @@ struct MergeParams {
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
-                              uint16_t* vr, int B, int L, int H, const RopeDev& rope, hipStream_t stream);
+                              uint16_t* vr, int B, int L, int H, const RopeDev& rope, const int32_t* lens,
+                              hipStream_t stream);
 hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
                               uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
                               const RopeDev& rope, hipStream_t stream);

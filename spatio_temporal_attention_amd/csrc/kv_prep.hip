@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_k_tiles_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ kf,
                                                           int* __restrict__ kexp, uint16_t* __restrict__ kt,
                                                           uint16_t* __restrict__ vr, int L, int H, int nt,
-                                                          RopeDev rope) {
+                                                          RopeDev rope, const int32_t* __restrict__ lens) {
   __shared__ __attribute__((aligned(16))) StageRows s;
   __shared__ float wmax[4];
   const int tile = blockIdx.x % nt;
@@ -168,15 +168,16 @@ __global__ __launch_bounds__(256) void bwd_k_tiles_kernel(const uint16_t* __rest
   const int b = bh / H;
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
+  const int valid = lens != nullptr ? min(max(lens[b], 0), L) : L;
   TileFrag f;
-  const float mk = load_tile(f, k, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid, L, 0);
+  const float mk = load_tile(f, k, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid, valid, 0);
   const int e = pow2_exponent_15(block_max(mk, wmax, tid));
   if (tid == 0) kexp[blockIdx.x] = e;
   store_row_tile_f16(kf + off, f, e, tid);
   stage_bf16(s, f, tid);
   __syncthreads();
   store_t_tile(kt + off, s, tid);
-  load_tile(f, v, b, h, tile, L, H, nullptr, tid, L, 0);
+  load_tile(f, v, b, h, tile, L, H, nullptr, tid, valid, 0);
   store_row_tile_bf16(vr + off, f, tid);
 }
 
@@ -255,11 +256,12 @@ hipError_t launch_kv_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kt, i
 }
 
 hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
-                              uint16_t* vr, int B, int L, int H, const RopeDev& rope, hipStream_t stream) {
+                              uint16_t* vr, int B, int L, int H, const RopeDev& rope, const int32_t* lens,
+                              hipStream_t stream) {
   int nt;
   dim3 grid;
   if (grid_of_tiles(B, L, H, nt, grid) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_k_tiles_kernel, grid, dim3(256), 0, stream, k, v, kf, kexp, kt, vr, L, H, nt, rope);
+  hipLaunchKernelGGL(bwd_k_tiles_kernel, grid, dim3(256), 0, stream, k, v, kf, kexp, kt, vr, L, H, nt, rope, lens);
   return hipGetLastError();
 }
 

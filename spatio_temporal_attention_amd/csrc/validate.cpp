@@ -62,30 +62,39 @@ size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
   return self_fwd_ws_layout(B, L, H, D, with_rope).total;
 }
 
-BwdWsLayout self_bwd_ws_layout(int B, int L, int H, int D) {
+BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
   BwdWsLayout w{};
-  if (check_dims(B, L, H, D) != WANATTN_OK) return w;
-  const size_t tiles = (size_t)B * H * (((size_t)L + 63) / 64);
-  const size_t tile_bytes = tiles * 64 * (size_t)D * 2;
+  if (check_dims(B, Lq, H, D) != WANATTN_OK || check_dims(B, Lk, H, D) != WANATTN_OK) return w;
+  const size_t qtiles = (size_t)B * H * (((size_t)Lq + 63) / 64);
+  const size_t ktiles = (size_t)B * H * (((size_t)Lk + 63) / 64);
+  const size_t qbytes = qtiles * 64 * (size_t)D * 2;
+  const size_t kbytes = ktiles * 64 * (size_t)D * 2;
   size_t at = 0;
   w.delta = at;
-  at = align256(at + (size_t)B * H * L * 4);
-  size_t* parts[] = {&w.qf, &w.qt, &w.dor, &w.dot, &w.kf, &w.kt, &w.vr};
-  for (size_t* part : parts) {
+  at = align256(at + (size_t)B * H * Lq * 4);
+  size_t* qparts[] = {&w.qf, &w.qt, &w.dor, &w.dot};
+  for (size_t* part : qparts) {
     *part = at;
-    at = align256(at + tile_bytes);
+    at = align256(at + qbytes);
+  }
+  size_t* kparts[] = {&w.kf, &w.kt, &w.vr};
+  for (size_t* part : kparts) {
+    *part = at;
+    at = align256(at + kbytes);
   }
   w.qexp = at;
-  at = align256(at + tiles * 4);
+  at = align256(at + qtiles * 4);
   w.kexp = at;
-  w.total = at + tiles * 4;
+  w.total = at + ktiles * 4;
   return w;
 }
 
 size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
   (void)with_rope;   // the same tiles serve both
-  return self_bwd_ws_layout(B, L, H, D).total;
+  return bwd_ws_layout(B, L, L, H, D).total;
 }
+
+size_t cross_bwd_ws_bytes(int B, int Lq, int Lk, int H, int D) { return bwd_ws_layout(B, Lq, Lk, H, D).total; }
 
 static int check_bf16(const void* p) {
   if (p == nullptr) return WANATTN_ERR_NULL;
@@ -185,6 +194,24 @@ int validate_self_bwd(const void* q, const void* k, const void* v, const void* o
   if (!aligned(lse, 4)) return WANATTN_ERR_ALIGN;
   if (table != nullptr && !aligned(table, 16)) return WANATTN_ERR_ALIGN;
   if (ws == nullptr || ws_bytes < self_bwd_ws_bytes(B, L, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
+int validate_cross_bwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
+                       const float* lse, const void* dout, const void* dq, const void* dk, const void* dv, int B,
+                       int Lq, int Lk, int H, int D, float scale, const void* ws, size_t ws_bytes) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return WANATTN_ERR_NULL;
+  WANATTN_TRY(check_dims(B, Lq, H, D));
+  WANATTN_TRY(check_dims(B, Lk, H, D));
+  WANATTN_TRY(check_scale(scale));
+  const void* bufs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : bufs) WANATTN_TRY(check_bf16(p));
+  if (!aligned(lse, 4)) return WANATTN_ERR_ALIGN;
+  if (k_lens != nullptr && !aligned(k_lens, 4)) return WANATTN_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < cross_bwd_ws_bytes(B, Lq, Lk, H, D)) return WANATTN_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
   return WANATTN_OK;
 }

@@ -35,8 +35,11 @@ size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);
 struct BwdWsLayout {
   size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, total;
 };
-BwdWsLayout self_bwd_ws_layout(int B, int L, int H, int D);
+// Query-side parts (Delta, qf, qt, dor, dot, qexp) over Lq tokens, key-side
+// parts (kf, kt, vr, kexp) over Lk.
+BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D);
 size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope);
+size_t cross_bwd_ws_bytes(int B, int Lq, int Lk, int H, int D);
 
 int validate_rope3d(const void* x, const void* y, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
                     const float* table);
@@ -55,6 +58,9 @@ int validate_partial_fwd(const void* q, const void* k, const void* v, const void
                          int k_offset, float scale, const void* ws, size_t ws_bytes);
 int validate_lse_merge(const void* const* o_parts, const float* const* lse_parts, int R, const void* o,
                        const float* lse, int B, int L, int H, int D);
+int validate_cross_bwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
+                       const float* lse, const void* dout, const void* dq, const void* dk, const void* dv, int B,
+                       int Lq, int Lk, int H, int D, float scale, const void* ws, size_t ws_bytes);
 int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
                        const float* lse, int B, int Lq, int Lk, int H, int D, float scale);
 

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libwanattn.so"
         assert n in wa._SIGNATURES, f"{n} has no binding"
@@ -205,4 +205,27 @@ def test_varlen_partial_merge_validation(lib):
     assert merge(parts=[P, ODD]) == ALIGN
     assert merge(o=None) == NULL
     assert merge(L=0) == SHAPE
+
+
+def test_cross_bwd_validation(lib):
+    """Every call below has at least one invalid argument, so nothing is launched."""
+    def cb(**kw):
+        a = dict(q=P, k=P, v=P, kl=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=2, Lq=100, Lk=512, H=2, D=128,
+                 scale=0.088, ws=P, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.wanattn_cross_bwd(a["q"], a["k"], a["v"], a["kl"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                     a["dv"], a["B"], a["Lq"], a["Lk"], a["H"], a["D"], a["scale"], a["ws"],
+                                     a["ws_bytes"], None)
+    assert cb(lse=None) == NULL
+    assert cb(dk=None) == NULL
+    assert cb(Lk=0) == SHAPE
+    assert cb(D=64) == UNSUP
+    assert cb(kl=P + 2) == ALIGN
+    assert cb(dv=ODD) == ALIGN
+    assert cb(ws=None) == WS
+    need = lib.wanattn_cross_bwd_workspace_bytes(2, 100, 512, 2, 128)
+    assert cb(ws_bytes=need - 1) == WS
+    # Delta [B, H, Lq] + 4 query-side and 3 key-side tile arrays + the two exponent arrays
+    qt, kt = 2 * 2 * 2, 2 * 2 * 8
+    assert need == (2 * 2 * 100 * 4 + 255) // 256 * 256 + 4 * qt * 16384 + 3 * kt * 16384 + 256 + kt * 4
 
