@@ -109,6 +109,7 @@ def bench_next_rows(wa, torch, synth, dev, rope):
       131,072-token query shard x a 131,072-token key/value shard, 5 heads, global RoPE positions,
       then the exact merge of the two hops' partial results;
     - the text cross-attention backward at the step's shape;
+    - the FP8 (e4m3) forward on the headline workload;
     - a joint video + image batch: a 720p clip (75,600 tokens) and one image frame (3,600 tokens)
       padded to 75,600, 40 heads, variable-length self-attention."""
     out = {}
@@ -146,6 +147,19 @@ def bench_next_rows(wa, torch, synth, dev, rope):
     out["cross_bwd"] = {"workload": "720p video tokens (75,600) over 512 text tokens (336 valid), 40 heads",
                         "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
     del q, do, tk, tv, o, ws, dq, dk, dv
+    # FP8 (e4m3) forward on the headline workload: 720p, 40 heads, 3D RoPE
+    L, H = 75600, 40
+    q, k, v = (torch.randn((1, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    table = wa.rope_table((21, 45, 80), rope, device=dev)
+    ws = torch.empty(wa.self_fwd_fp8_workspace_bytes(1, L, H), dtype=torch.uint8, device=dev)
+    o, lse = torch.empty_like(q), torch.empty((1, H, L), dtype=torch.float32, device=dev)
+    ms = _time(lambda: wa.self_fwd_fp8(q, k, v, grid=(21, 45, 80), table=table, rope=rope, out=o, lse=lse,
+                                       workspace=ws), reps=2)
+    flop = 4.0 * H * L * L * 128
+    out["fp8_fwd"] = {"workload": "720p self-attention (75,600 tokens, 40 heads, 3D RoPE), e4m3 operands",
+                      "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                      "pct_fp8_peak": round(100.0 * flop / (ms * 1e-3) / 5.0e15, 2)}
+    del q, k, v, o, ws
     L, H = 75600, 40
     q, k, v = (torch.randn((2, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
     lens = torch.tensor([L, 3600], dtype=torch.int32, device=dev)

@@ -139,6 +139,28 @@ int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float
                      void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * FP8 self-attention forward: the operation of wanattn_self_fwd (same
+ * arguments) computed with OCP fp8 e4m3 products at twice the bf16 MFMA rate
+ * (FP8 attention is named without a recipe in [lit619] Tags; the recipe is
+ * this library's).  The rotated queries, rotated keys and values are scaled
+ * per 64-token tile of each (b, h) by the power of two that puts the tile's
+ * largest |element| in [128, 256) and rounded to e4m3 (RNE, saturating at
+ * +-448); both products run on fp8 MFMAs whose scale operands undo the powers
+ * of two exactly; P is rounded to e4m3 for P.V, while the softmax statistics
+ * and LSE use fp32 P.  Accuracy: O is the attention of the dequantized inputs
+ * up to P's e4m3 rounding (relative L2 of a few 1e-2 on flat rows); LSE to
+ * ~1e-4.  Workspace (required, 16-byte aligned):
+ * wanattn_self_fwd_fp8_workspace_bytes(B, L, H, D): e4m3 K and V^T tiles
+ * ([B, H, ceil(L/64)] x 8 KB each) and their int32 exponents.
+ * ------------------------------------------------------------------------- */
+size_t wanattn_self_fwd_fp8_workspace_bytes(int B, int L, int H, int D);
+
+int wanattn_self_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int L, int H, int D,
+                         wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Self-attention backward (training, [notes] 3. Training: bf16; the formulas
  * are the calculus of the forward above).  Given o and lse from
  * wanattn_self_fwd and the output gradient dout:

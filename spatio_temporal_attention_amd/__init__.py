@@ -73,6 +73,8 @@ _SIGNATURES = {
     "wanattn_partial_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, Grid, Rope, _vp, _i, _i, _f, _vp, _sz,
                                  _vp]),
     "wanattn_lse_merge": (_i, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "wanattn_self_fwd_fp8_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "wanattn_self_fwd_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, Grid, Rope, _vp, _f, _vp, _sz, _vp]),
     "wanattn_cross_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "wanattn_cross_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz,
                                _vp]),
@@ -388,4 +390,34 @@ def cross_bwd(q, k, v, k_lens, o, lse, dout, scale=None, workspace=None, dq=None
                                    _ptr(dk), _ptr(dv), B, Lq, Lk, H, D, scale, _ptr(ws),
                                    nbytes if ws is None else ws.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+def self_fwd_fp8_workspace_bytes(B, L, H, D=HEAD_DIM) -> int:
+    return int(lib().wanattn_self_fwd_fp8_workspace_bytes(B, L, H, D))
+
+
+def self_fwd_fp8(q, k, v, grid=None, table=None, rope=None, scale=None, out=None, lse=None, workspace=None,
+                 want_lse=True):
+    """FP8 (e4m3) self-attention forward with optional 3D RoPE.  Returns (o, lse)."""
+    torch = _torch()
+    _need(q, torch.bfloat16, "q")
+    B, L, H, D = q.shape
+    _need(k, torch.bfloat16, "k", q.shape)
+    _need(v, torch.bfloat16, "v", q.shape)
+    if table is not None:
+        _need(table, torch.float32, "table")
+    o = torch.empty_like(q) if out is None else out
+    _need(o, torch.bfloat16, "out", q.shape)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (B, H, L))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = self_fwd_fp8_workspace_bytes(B, L, H, D)
+    ws = _workspace(nbytes, q.device, workspace)
+    g = _grid(grid if grid is not None else (1, 1, L))
+    _check(lib().wanattn_self_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, L, H, D, g, _rope(rope),
+                                      _ptr(table), scale, _ptr(ws), nbytes if ws is None else ws.numel(),
+                                      _stream(q.device)))
+    return o, lse
 

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libwanattn.so")
 
-SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_bwd.hip", "merge.hip", "validate.cpp"]
+SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "merge.hip",
+           "validate.cpp"]
 ARCH = "gfx950"
 
 

@@ -133,6 +133,39 @@ WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, vo
   return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, nullptr, 0, 0, (hipStream_t)stream);
 }
 
+WANATTN_API size_t wanattn_self_fwd_fp8_workspace_bytes(int B, int L, int H, int D) {
+  return self_fwd_fp8_ws_layout(B, L, H, D).total;
+}
+
+WANATTN_API int wanattn_self_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int L,
+                                     int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  // Same arguments as wanattn_self_fwd; only the workspace size differs.
+  const size_t need = self_fwd_fp8_ws_layout(B, L, H, D).total;
+  const int rc = validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, (size_t)-1);
+  if (rc != WANATTN_OK) return rc;
+  if (need == 0 || ws_bytes < need) return WANATTN_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const RopeDev rope = make_rope(g, r, table);
+  const Fp8WsLayout w = self_fwd_fp8_ws_layout(B, L, H, D);
+  uint8_t* base = (uint8_t*)ws;
+  int e = hip_status(launch_kv8_tiles((const uint16_t*)k, (const uint16_t*)v, base + w.k8, (int*)(base + w.kexp),
+                                      base + w.v8, (int*)(base + w.vexp), B, L, H, rope, s));
+  if (e != WANATTN_OK) return e;
+  FwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.rope = rope;
+  p.B = B;
+  p.Lq = L;
+  p.Lk = L;
+  p.H = H;
+  p.scale_log2 = scale * LOG2E_F;
+  return hip_status(launch_attn_fwd_fp8(p, base + w.k8, (const int*)(base + w.kexp), base + w.v8,
+                                        (const int*)(base + w.vexp), s));
+}
+
 WANATTN_API int wanattn_self_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                         const int32_t* seq_lens, int B, int L, int H, int D, wanattn_grid g,
                                         wanattn_rope r, const float* table, float scale, void* ws, size_t ws_bytes,

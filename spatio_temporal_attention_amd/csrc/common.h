@@ -27,6 +27,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -41,6 +42,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   f32x2 v = {a, b};
   bf16x2 p = __builtin_convertvector(v, bf16x2);
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Four fp32 -> packed OCP fp8 e4m3 (round to nearest even), byte 0 = a, saturated
+// to +-448 so that out-of-range values never become NaN.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  constexpr float M = 448.f;
+  a = fminf(fmaxf(a, -M), M);
+  b = fminf(fmaxf(b, -M), M);
+  c = fminf(fmaxf(c, -M), M);
+  d = fminf(fmaxf(d, -M), M);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
 
 // Two fp32 -> packed fp16 (round to nearest even).

@@ -73,6 +73,12 @@ struct MergeParams {
 };
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
+// FP8 forward: K as e4m3 row tiles [64][128] and V as e4m3 V^T tiles [128][64]
+// (8 KB each, key order kappa), with int32 exponents per tile.
+hipError_t launch_kv8_tiles(const uint16_t* k, const uint16_t* v, uint8_t* k8, int* kexp, uint8_t* v8, int* vexp,
+                            int B, int L, int H, const RopeDev& rope, hipStream_t stream);
+hipError_t launch_attn_fwd_fp8(const FwdParams& p, const uint8_t* k8, const int* kexp, const uint8_t* v8,
+                               const int* vexp, hipStream_t stream);
 hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
                               uint16_t* vr, int B, int L, int H, const RopeDev& rope, const int32_t* lens,
                               hipStream_t stream);

@@ -62,6 +62,18 @@ size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
   return self_fwd_ws_layout(B, L, H, D, with_rope).total;
 }
 
+Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D) {
+  Fp8WsLayout w{};
+  if (check_dims(B, L, H, D) != WANATTN_OK) return w;
+  const size_t tiles = (size_t)B * H * (((size_t)L + 63) / 64);
+  w.k8 = 0;
+  w.v8 = align256(tiles * 64 * (size_t)D);
+  w.kexp = align256(w.v8 + tiles * 64 * (size_t)D);
+  w.vexp = align256(w.kexp + tiles * 4);
+  w.total = w.vexp + tiles * 4;
+  return w;
+}
+
 BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
   BwdWsLayout w{};
   if (check_dims(B, Lq, H, D) != WANATTN_OK || check_dims(B, Lk, H, D) != WANATTN_OK) return w;

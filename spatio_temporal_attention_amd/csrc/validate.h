@@ -29,6 +29,12 @@ struct FwdWsLayout {
 };
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope);
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);
+// FP8 forward workspace: K and V^T e4m3 tiles ([B, H, ceil(L/64)] x 8 KB each), then
+// their int32 exponents; each part on a 256-byte boundary.
+struct Fp8WsLayout {
+  size_t k8, v8, kexp, vexp, total;
+};
+Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D);
 // Backward workspace: Delta (fp32 [B, H, L]), then the prep passes' tiles
 // (each [B, H, ceil(L/64)] x 16 KB) and the two exponent arrays (int32 per
 // tile); each part starts on a 256-byte boundary.

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libwanattn.so"
         assert n in wa._SIGNATURES, f"{n} has no binding"
@@ -228,4 +228,22 @@ def test_cross_bwd_validation(lib):
     # Delta [B, H, Lq] + 4 query-side and 3 key-side tile arrays + the two exponent arrays
     qt, kt = 2 * 2 * 2, 2 * 2 * 8
     assert need == (2 * 2 * 100 * 4 + 255) // 256 * 256 + 4 * qt * 16384 + 3 * kt * 16384 + 256 + kt * 4
+
+
+def test_fp8_validation(lib):
+    """Every call below has at least one invalid argument, so nothing is launched."""
+    def f8(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P, scale=0.088, ws=P,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.wanattn_self_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["L"], a["H"], a["D"],
+                                        a["g"], a["r"], a["table"], a["scale"], a["ws"], a["ws_bytes"], None)
+    need = lib.wanattn_self_fwd_fp8_workspace_bytes(1, 320, 2, 128)
+    assert need == 2 * 10 * 8192 + 256 + 4 * 10   # K and V^T e4m3 tiles, then the two exponent arrays
+    assert f8(ws_bytes=need - 1) == WS
+    assert f8(ws=None) == WS
+    assert f8(q=None) == NULL
+    assert f8(L=321) == SHAPE
+    assert f8(D=64) == UNSUP
+    assert f8(scale=float("inf")) == UNSUP
 
