@@ -84,8 +84,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = logical % p.n_tiles;
   const int bh = logical / p.n_tiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
+  const int h = bh / p.B;
   const int nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;     // query tiles
   const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;    // key tiles
   const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
@@ -241,8 +241,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qb = logical % p.n_tiles;
   const int bh = logical / p.n_tiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
+  const int h = bh / p.B;
   const int nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;     // query tiles
   const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;    // key tiles
   const int64_t tile0 = (int64_t)(b * p.H + h) * nt;

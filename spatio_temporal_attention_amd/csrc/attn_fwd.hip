@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = logical % p.n_qtiles;
   const int bh = logical / p.n_qtiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
+  const int h = bh / p.B;
 
   int n_keys = p.Lk;
   if (p.k_lens != nullptr) n_keys = min(max(p.k_lens[b], 0), p.Lk);

@@ -174,8 +174,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = logical % p.n_qtiles;
   const int bh = logical / p.n_qtiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
+  const int h = bh / p.B;
   const int n_keys = p.Lk;
   const int64_t q_row_stride = (int64_t)p.H * HD;
   const uint16_t* qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * HD;

@@ -304,7 +304,9 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // XCD-aware workgroup order: the hardware deals workgroups round-robin over
 // the 8 XCDs (each with its own L2).  Return a logical index such that every
 // XCD receives a contiguous range of logical indices, so workgroups that share
-// K/V (same batch and head) run on the same XCD.
+// K/V (same batch and head) run on the same XCD.  Kernels order the logical
+// index as ((head, batch), tile) with the batch item innermost, so that items
+// of unequal work (variable lengths) spread evenly over the XCDs.
 __device__ __forceinline__ int xcd_remap(int wg, int total) {
   constexpr int NXCD = 8;
   const int q = total / NXCD;
