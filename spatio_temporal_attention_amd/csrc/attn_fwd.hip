@@ -50,7 +50,15 @@ constexpr float RESCALE_SLACK = 8.0f;     // log2 units: P stays <= 256 between 
 
 template <bool POS_SCALE, bool F16, bool TILED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE_ELEMS];   // [buffer][K|V]
+  // Two K and two V buffers as four separate objects: every access in the
+  // (two-way unrolled) loop names its buffer statically, which lets the
+  // compiler see that the ds_reads of one buffer do not depend on the DMA
+  // copies in flight into another (otherwise each LDS read would wait for
+  // all of them).
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[TILE_ELEMS];
   __shared__ float qmax_s[FWD_WAVES];                                        // F16: max |q~| per wave
 
   const int tid = threadIdx.x;
@@ -245,23 +253,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(TILED ? p.kt + tile0 * TILE_ELEMS : p.k, bytes);
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(TILED ? p.vt + tile0 * TILE_ELEMS : p.v, bytes);
-    // Stage tile t of K (V) into K (V) buffer `buf`.
-    auto stage_k = [&](int buf, int t) {
+    // Stage tile t of K (V) into the LDS buffer `dst`.
+    auto stage_k = [&](uint16_t* dst, int t) {
       if (TILED) {
         const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) buf_dma16(krs, koff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][0], wv, i));
+        for (int i = 0; i < 4; ++i) buf_dma16(krs, koff[i], soff, tile_lds_block<FWD_WAVES>(dst, wv, i));
       } else {
-        tile_dma(smem[buf][0], kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
+        tile_dma(dst, kbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
       }
     };
-    auto stage_v = [&](int buf, int t) {
+    auto stage_v = [&](uint16_t* dst, int t) {
       if (TILED) {
         const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) buf_dma16(vrs, voff[i], soff, tile_lds_block<FWD_WAVES>(smem[buf][1], wv, i));
+        for (int i = 0; i < 4; ++i) buf_dma16(vrs, voff[i], soff, tile_lds_block<FWD_WAVES>(dst, wv, i));
       } else {
-        tile_dma(smem[buf][1], vbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
+        tile_dma(dst, vbase, q_row_stride, t * FWD_BC, n_keys, wv, lane);
       }
     };
     // Software pipeline: iteration t computes the scores of tile t+1 (MFMA)
@@ -269,41 +277,72 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
     // one tile ahead of V: iteration t copies K(t+2) and V(t+1) into the
     // buffers K(t) and V(t-1) have left.  A tile's exponent is loaded with
     // its copies, so the wait that ends the previous iteration covers it.
-    stage_k(0, 0);
-    stage_v(0, 0);
+    stage_k(k_lds0, 0);
+    stage_v(v_lds0, 0);
     int e_cur = F16 ? kexp[0] : 0;
     int e_nxt = 0;
     if (n_tiles > 1) {
-      stage_k(1, 1);
+      stage_k(k_lds1, 1);
       if (F16) e_nxt = kexp[1];
     }
     wait_vmem();
     __syncthreads();
-    f32x16 s_cur[2];
-    scores(smem[0][0], s_cur);
+    f32x16 s_a[2], s_b[2];
+    scores(k_lds0, s_a);
     __syncthreads();   // K buffer 0 is refilled in iteration 0
     const int last = n_tiles - 1;
-    for (int t = 0; t < last; ++t) {
+    // Iteration t (parity P = t & 1): scores of tile t are in s_in, K(t+1)
+    // is in K buffer 1-P, V(t) in V buffer P; K(t+2) goes into K buffer P
+    // and V(t+1) into V buffer 1-P.
+    auto iteration = [&](auto parity, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2]) {
+      const int P = parity;
+      uint16_t* const k_fill = P ? k_lds1 : k_lds0;
+      const uint16_t* const k_next = P ? k_lds0 : k_lds1;
+      const uint16_t* const v_cur = P ? v_lds1 : v_lds0;
+      uint16_t* const v_fill = P ? v_lds0 : v_lds1;
       int e_nxt2 = 0;
       if (t + 2 < n_tiles) {
-        stage_k(t & 1, t + 2);
+        stage_k(k_fill, t + 2);
         if (F16) e_nxt2 = kexp[t + 2];
       }
-      stage_v((t + 1) & 1, t + 1);
-      f32x16 s_nxt[2];
-      softmax_pv(std::false_type{}, std::true_type{}, s_cur, smem[t & 1][1], t, e_cur, smem[(t + 1) & 1][0], s_nxt);
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
+      stage_v(v_fill, t + 1);
+      softmax_pv(std::false_type{}, std::true_type{}, s_in, v_cur, t, e_cur, k_next, s_out);
       e_cur = e_nxt;
       e_nxt = e_nxt2;
       wait_vmem();
       __syncthreads();
-    }
+    };
     // Only the last tile can be partial.
-    if (n_keys % FWD_BC != 0)
-      softmax_pv(std::true_type{}, std::false_type{}, s_cur, smem[last & 1][1], last, e_cur, nullptr, s_cur);
-    else
-      softmax_pv(std::false_type{}, std::false_type{}, s_cur, smem[last & 1][1], last, e_cur, nullptr, s_cur);
+    auto finish = [&](f32x16 (&s)[2], const uint16_t* vs) {
+      if (n_keys % FWD_BC != 0)
+        softmax_pv(std::true_type{}, std::false_type{}, s, vs, last, e_cur, nullptr, s);
+      else
+        softmax_pv(std::false_type{}, std::false_type{}, s, vs, last, e_cur, nullptr, s);
+    };
+    if constexpr (TILED) {
+      // Unrolled by two: the buffer parity is a compile-time constant.
+      int t = 0;
+      for (; t + 1 < last; t += 2) {
+        iteration(std::integral_constant<int, 0>{}, t, s_a, s_b);
+        iteration(std::integral_constant<int, 1>{}, t + 1, s_b, s_a);
+      }
+      if (t < last) {
+        iteration(std::integral_constant<int, 0>{}, t, s_a, s_b);
+        finish(s_b, v_lds1);
+      } else {
+        finish(s_a, v_lds0);
+      }
+    } else {
+      // Short key sets (text context): a plain loop with the parity at run
+      // time (the per-lane addressing of the row-major copies leaves no
+      // registers for a second copy of the body).
+      for (int t = 0; t < last; ++t) {
+        iteration(t & 1, t, s_a, s_b);
+        s_a[0] = s_b[0];
+        s_a[1] = s_b[1];
+      }
+      finish(s_a, (last & 1) ? v_lds1 : v_lds0);
+    }
   }
 
   // ---- epilogue: O = O / l (bf16), LSE = ln sum exp(s) = ln2 * (m + log2 l)
