@@ -70,9 +70,20 @@ __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* t
 // KMASK: keys j >= k_lens[b] get P = 0 (cross-attention key padding).
 template <bool KMASK>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE_ELEMS];   // [buf][Q fp16 | (Rq)^T | dO | dO^T]
-  __shared__ float lse2_s[2][TILE_ROWS];                                      // LSE * log2 e (+inf: no row)
-  __shared__ float delta_s[2][TILE_ROWS];
+  // Two buffers of the four query-side tiles (Q fp16 rows, (Rq)^T, dO rows,
+  // dO^T) and of the row statistics, each a separate object named
+  // statically in the two-way unrolled loop: LDS reads of one buffer then do
+  // not wait for the copies in flight into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t dot_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t dot_lds1[TILE_ELEMS];
+  __shared__ float lse2_s0[TILE_ROWS], lse2_s1[TILE_ROWS];     // LSE * log2 e (+inf: no row)
+  __shared__ float delta_s0[TILE_ROWS], delta_s1[TILE_ROWS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,45 +135,72 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + tile0 * TILE_ELEMS, bytes);
   const int* qexp = p.qexp + tile0;
 
-  auto stage = [&](int buf, int t) {
+  struct Buf {
+    uint16_t* q;
+    uint16_t* qt;
+    uint16_t* dO;
+    uint16_t* dOt;
+    float* lse2;
+    float* delta;
+  };
+  const Buf buf0{q_lds0, qt_lds0, do_lds0, dot_lds0, lse2_s0, delta_s0};
+  const Buf buf1{q_lds1, qt_lds1, do_lds1, dot_lds1, lse2_s1, delta_s1};
+
+  auto stage = [&](const Buf& dst, int t) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      buf_dma16(qfr, roff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][0], wv, i));
-      buf_dma16(qtr, toff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][1], wv, i));
-      buf_dma16(dor, roff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][2], wv, i));
-      buf_dma16(dotr, toff[i], soff, tile_lds_block<DKDV_WAVES>(tiles[buf][3], wv, i));
-    }
-    if (tid < TILE_ROWS) {
-      // rows past Lq, and rows with no valid key (LSE = -inf), contribute nothing
-      const int i = t * TILE_ROWS + tid;
-      const float l = (i < p.Lq) ? lse_row[i] : -INFINITY;
-      lse2_s[buf][tid] = (l > -INFINITY) ? l * LOG2E : INFINITY;
-    } else if (tid < 2 * TILE_ROWS) {
-      const int i = t * TILE_ROWS + tid - TILE_ROWS;
-      delta_s[buf][tid - TILE_ROWS] = (i < p.Lq) ? delta_row[i] : 0.f;
+      buf_dma16(qfr, roff[i], soff, tile_lds_block<DKDV_WAVES>(dst.q, wv, i));
+      buf_dma16(qtr, toff[i], soff, tile_lds_block<DKDV_WAVES>(dst.qt, wv, i));
+      buf_dma16(dor, roff[i], soff, tile_lds_block<DKDV_WAVES>(dst.dO, wv, i));
+      buf_dma16(dotr, toff[i], soff, tile_lds_block<DKDV_WAVES>(dst.dOt, wv, i));
     }
   };
+  // Row statistics of query tile t: threads 0..63 read LSE, 64..127 Delta,
+  // into a register (published to LDS by store_stats once loaded).
+  auto load_stats = [&](int t) {
+    float x = 0.f;
+    if (tid < TILE_ROWS) {
+      const int i = t * TILE_ROWS + tid;
+      x = (i < p.Lq) ? lse_row[i] : -INFINITY;
+    } else if (tid < 2 * TILE_ROWS) {
+      const int i = t * TILE_ROWS + tid - TILE_ROWS;
+      x = (i < p.Lq) ? delta_row[i] : 0.f;
+    }
+    return x;
+  };
+  auto store_stats = [&](const Buf& dst, float x) {
+    // rows past Lq, and rows with no valid key (LSE = -inf), contribute nothing
+    if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
+    else if (tid < 2 * TILE_ROWS) dst.delta[tid - TILE_ROWS] = x;
+  };
 
-  // A tile's exponent is loaded with its copies, so the wait that ends the
-  // previous tile covers it.
-  stage(0, 0);
-  int e_q = qexp[0];
-  wait_vmem();
+  // A tile's exponent and statistics are loaded with its copies, so the
+  // wait that ends the previous tile covers them.
+  int e_q;
+  {
+    const float st = load_stats(0);
+    stage(buf0, 0);
+    e_q = qexp[0];
+    wait_vmem();
+    store_stats(buf0, st);
+  }
   __syncthreads();
 
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
+  // Query tile t with parity P = t & 1: tile t in buffer P, tile t+1 copied
+  // into buffer 1-P.
+  auto iteration = [&](auto parity, int t) {
+    constexpr int P = decltype(parity)::value;
+    const Buf& cur = P ? buf1 : buf0;
+    const Buf& nxt = P ? buf0 : buf1;
     const bool has_next = t + 1 < nt;
     int e_q_next = 0;
+    float st = 0.f;
     if (has_next) {
-      stage(buf ^ 1, t + 1);
+      st = load_stats(t + 1);
+      stage(nxt, t + 1);
       e_q_next = qexp[t + 1];
     }
-    const uint16_t* qs = tiles[buf][0];
-    const uint16_t* qts = tiles[buf][1];
-    const uint16_t* dos = tiles[buf][2];
-    const uint16_t* dots = tiles[buf][3];
     const float g = ldexpf(p.scale_log2, e_q + e_k);
 
     bf16x8 pf[4], dsf[4];
@@ -171,17 +209,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        s_acc = mfma32_f16(lds_row_frag(qs, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-        dp_acc = mfma32(lds_row_frag(dos, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
+        s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
+        dp_acc = mfma32(lds_row_frag(cur.dO, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
       }
       float pv[16], dsv[16];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int r = qb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);   // query row in the tile
-        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2_s[buf][r]));
+        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -cur.lse2[r]));
         if (KMASK && !key_live) pe = 0.f;
         pv[jj] = pe;
-        dsv[jj] = pe * (dp_acc[jj] - delta_s[buf][r]);
+        dsv[jj] = pe * (dp_acc[jj] - cur.delta[r]);
       }
       pf[2 * qb] = pack_acc8(pv);
       pf[2 * qb + 1] = pack_acc8(pv + 8);
@@ -192,15 +230,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
       for (int qg = 0; qg < 4; ++qg) {
-        dv_acc[d] = mfma32(lds_vt_frag(dots, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
-        dk_acc[d] = mfma32(lds_vt_frag(qts, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
+        dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
+        dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
       }
     }
 
-    if (has_next) wait_vmem();
+    if (has_next) {
+      wait_vmem();
+      store_stats(nxt, st);
+    }
     __syncthreads();
     e_q = e_q_next;
+  };
+  int t = 0;
+  for (; t + 1 < nt; t += 2) {
+    iteration(std::integral_constant<int, 0>{}, t);
+    iteration(std::integral_constant<int, 1>{}, t + 1);
   }
+  if (t < nt) iteration(std::integral_constant<int, 0>{}, t);
 
   if (key_ok) {
     TokenPos pos{0, 0, 0};

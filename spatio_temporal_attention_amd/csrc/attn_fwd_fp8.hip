@@ -162,7 +162,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
                                                               const int* __restrict__ kexp_all,
                                                               const uint8_t* __restrict__ v8,
                                                               const int* __restrict__ vexp_all) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][F8_TILE_BYTES];   // [buffer][K | V^T]
+  // Two K and two V^T buffers as separate objects, each named statically in
+  // the unrolled loop, so LDS reads do not wait for the copies in flight
+  // into the other buffers.
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds0[F8_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds1[F8_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds0[F8_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds1[F8_TILE_BYTES];
   __shared__ float qmax_s[F8_WAVES];
 
   const int tid = threadIdx.x;
@@ -322,56 +328,70 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
     const uint32_t bytes = (uint32_t)nkt * F8_TILE_BYTES;
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(k8 + tile0 * F8_TILE_BYTES, bytes);
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(v8 + tile0 * F8_TILE_BYTES, bytes);
-    auto stage_k = [&](int buf, int t) {
+    auto stage_k = [&](uint8_t* dst, int t) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        buf_dma16(krs, koff[c], (uint32_t)t * F8_TILE_BYTES, smem[buf][0] + 2048 * wv + 1024 * c);
+      for (int c = 0; c < 2; ++c) buf_dma16(krs, koff[c], (uint32_t)t * F8_TILE_BYTES, dst + 2048 * wv + 1024 * c);
     };
-    auto stage_v = [&](int buf, int t) {
+    auto stage_v = [&](uint8_t* dst, int t) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        buf_dma16(vrs, voff[c], (uint32_t)t * F8_TILE_BYTES, smem[buf][1] + 2048 * wv + 1024 * c);
+      for (int c = 0; c < 2; ++c) buf_dma16(vrs, voff[c], (uint32_t)t * F8_TILE_BYTES, dst + 2048 * wv + 1024 * c);
     };
     // Software pipeline as in attn_fwd.hip: scores of tile t+1 with the softmax of tile t.
-    stage_k(0, 0);
-    stage_v(0, 0);
+    stage_k(k_lds0, 0);
+    stage_v(v_lds0, 0);
     int ek_cur = kexp[0], ev_cur = vexp[0];
     int ek_nxt = 0, ev_nxt = 0;
     if (n_tiles > 1) {
-      stage_k(1, 1);
+      stage_k(k_lds1, 1);
       ek_nxt = kexp[1];
       ev_nxt = vexp[1];
     }
     wait_vmem();
     __syncthreads();
-    f32x16 s_cur[2];
-    scores(smem[0][0], ek_cur, s_cur);
+    f32x16 s_a[2], s_b[2];
+    scores(k_lds0, ek_cur, s_a);
     __syncthreads();
     const int last = n_tiles - 1;
-    for (int t = 0; t < last; ++t) {
+    // Iteration t (parity P = t & 1): K(t+1) in K buffer 1-P, V(t) in V
+    // buffer P; K(t+2) goes into K buffer P, V(t+1) into V buffer 1-P.
+    auto iteration = [&](auto parity, int t, f32x16 (&s_in)[2], f32x16 (&s_out)[2]) {
+      constexpr int P = decltype(parity)::value;
+      uint8_t* const k_fill = P ? k_lds1 : k_lds0;
+      const uint8_t* const k_next = P ? k_lds0 : k_lds1;
+      const uint8_t* const v_cur = P ? v_lds1 : v_lds0;
+      uint8_t* const v_fill = P ? v_lds0 : v_lds1;
       int ek_nxt2 = 0, ev_nxt2 = 0;
       if (t + 2 < n_tiles) {
-        stage_k(t & 1, t + 2);
+        stage_k(k_fill, t + 2);
         ek_nxt2 = kexp[t + 2];
         ev_nxt2 = vexp[t + 2];
       }
-      stage_v((t + 1) & 1, t + 1);
-      f32x16 s_nxt[2];
-      softmax_pv(std::false_type{}, std::true_type{}, s_cur, smem[t & 1][1], t, ev_cur, smem[(t + 1) & 1][0], ek_nxt,
-                 s_nxt);
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
+      stage_v(v_fill, t + 1);
+      softmax_pv(std::false_type{}, std::true_type{}, s_in, v_cur, t, ev_cur, k_next, ek_nxt, s_out);
       ek_cur = ek_nxt;
       ev_cur = ev_nxt;
       ek_nxt = ek_nxt2;
       ev_nxt = ev_nxt2;
       wait_vmem();
       __syncthreads();
+    };
+    auto finish = [&](f32x16 (&sc)[2], const uint8_t* vbuf) {
+      if (n_keys % F8_BC != 0)
+        softmax_pv(std::true_type{}, std::false_type{}, sc, vbuf, last, ev_cur, nullptr, 0, sc);
+      else
+        softmax_pv(std::false_type{}, std::false_type{}, sc, vbuf, last, ev_cur, nullptr, 0, sc);
+    };
+    int t = 0;
+    for (; t + 1 < last; t += 2) {
+      iteration(std::integral_constant<int, 0>{}, t, s_a, s_b);
+      iteration(std::integral_constant<int, 1>{}, t + 1, s_b, s_a);
     }
-    if (n_keys % F8_BC != 0)
-      softmax_pv(std::true_type{}, std::false_type{}, s_cur, smem[last & 1][1], last, ev_cur, nullptr, 0, s_cur);
-    else
-      softmax_pv(std::false_type{}, std::false_type{}, s_cur, smem[last & 1][1], last, ev_cur, nullptr, 0, s_cur);
+    if (t < last) {
+      iteration(std::integral_constant<int, 0>{}, t, s_a, s_b);
+      finish(s_b, v_lds1);
+    } else {
+      finish(s_a, v_lds0);
+    }
   }
 
   const float l_tot = xor32_sum(l_run);
