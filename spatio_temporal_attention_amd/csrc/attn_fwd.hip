@@ -31,7 +31,8 @@
 //    per clock and would make the loop LDS-bound.  Cross-attention (a short
 //    text context, no workspace) keeps the transpose read;
 //  * online softmax in fp32 in the log2 domain (scale * log2 e folded in),
-//    with lazy rescaling of O and l (only when a row max grows by > 2^8);
+//    with lazy rescaling of O and l: no per-tile max, m moves only when a
+//    row's partial sum of P would exceed 2^16;
 //  * workgroups are ordered head-major and XCD-aware so that the resident
 //    workgroups of one XCD walk the same head's K/V through its L2.
 #include <type_traits>
@@ -46,7 +47,7 @@ namespace {
 constexpr int FWD_WAVES = 4;
 constexpr int FWD_BR = 32 * FWD_WAVES;   // query rows per workgroup
 constexpr int FWD_BC = TILE_ROWS;         // keys per tile
-constexpr float RESCALE_SLACK = 8.0f;     // log2 units: P stays <= 256 between rescales
+constexpr float PSUM_LIMIT = 65536.0f;    // largest partial row sum of P kept without a rescale
 
 template <bool POS_SCALE, bool F16, bool TILED>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
@@ -190,44 +191,56 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
         sv[kb][j] = x;
       }
     }
-    float mx = sv[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
-    mx = xor32_max(mx);
-    if (POS_SCALE) mx *= g;   // max(s) * g == max(s * g) for g > 0
 
-    // Lazy rescaling: the running max only moves when some row's tile max
-    // exceeds it by more than RESCALE_SLACK (log2 units), so p <= 2^SLACK and
-    // the O/l rescale is skipped on almost every tile.  Exact either way: the
-    // final O / l and LSE = m + log2 l use the max that was applied.
-    if (__any(mx > m_run + RESCALE_SLACK)) {
+    if (NEXT) scores(next_ks, s_nxt);
+
+    // P = 2^(s - m) against the running max m, in fp32 (l sums these; P is
+    // rounded to bf16, RNE, only for the P V product: summing the rounded
+    // values instead would move LSE by up to ~2^-9 when few keys dominate).
+    bf16x8 pf[4];
+    float psum;
+    auto exps = [&]() {
+      float part[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[16];
+        part[kb] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], g, -m_run));
+          else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
+          part[kb] += pv[j];
+        }
+        pf[2 * kb] = pack_acc8(pv);
+        pf[2 * kb + 1] = pack_acc8(pv + 8);
+      }
+      psum = part[0] + part[1];
+    };
+    exps();
+
+    // Lazy rescaling without a per-tile max: m only has to keep P finite
+    // and bounded.  While every row's partial sum (32 of its P) stays <=
+    // PSUM_LIMIT = 2^16, so does every P, and the tile is kept as computed;
+    // scores up to m + 11 (log2 units) always stay on this path.  Otherwise
+    // (a larger score, the first tile with m = -inf, or a non-finite sum)
+    // the exact tile max is taken, m moves up to it, O and l are rescaled
+    // and P is recomputed.  Exact either way: the final O / l and
+    // LSE = m + log2 l use the m that was applied.
+    if (__any(!(psum <= PSUM_LIMIT))) {
+      float mx = sv[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
+      mx = xor32_max(mx);
+      if (POS_SCALE) mx *= g;   // max(s) * g == max(s * g) for g > 0
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m was -inf
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
-    }
-
-    if (NEXT) scores(next_ks, s_nxt);
-
-    // P in bf16 (RNE) for PV; l sums P in fp32 (summing the rounded values
-    // instead would move LSE by up to ~2^-9 when few keys dominate).
-    float psum = 0.f;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], g, -m_run));
-        else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
-        psum += pv[j];
-      }
-      pf[2 * kb] = pack_acc8(pv);
-      pf[2 * kb + 1] = pack_acc8(pv + 8);
+      exps();
     }
     l_run += psum;
 
