@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t qtr = tile_rsrc(p.qt + tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t dor = tile_rsrc(p.dor + tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + tile0 * TILE_ELEMS, bytes);
-  const int* qexp = p.qexp + tile0;
+  const_i32* qexp = const_ptr(p.qexp + tile0);   // scalar loads
 
   struct Buf {
     uint16_t* q;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t kfr = tile_rsrc(p.kf + ktile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t ktr = tile_rsrc(p.kt + ktile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t vrr = tile_rsrc(p.vr + ktile0 * TILE_ELEMS, bytes);
-  const int* kexp = p.kexp + ktile0;
+  const_i32* kexp = const_ptr(p.kexp + ktile0);   // scalar loads
 
   auto stage = [&](int buf, int t) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);

@@ -147,11 +147,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   for (int d = 0; d < 4; ++d) o_acc[d] = f32x16{};
   float m_run = -INFINITY;   // running max of scale*log2e*s (this lane's row)
   float l_run = 0.f;         // this lane's partial exp-sum (the other half holds the rest)
-  // e_t of each key tile, read through the constant address space: the
-  // array is not written during the kernel, and the loads (uniform index)
-  // become scalar loads into SGPRs.
-  using const_int = const __attribute__((address_space(4))) int;
-  const_int* kexp = F16 ? (const_int*)(p.kexp + tile0) : nullptr;
+  // e_t of each key tile (scalar loads)
+  const_i32* kexp = F16 ? const_ptr(p.kexp + tile0) : nullptr;
 
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 

@@ -36,7 +36,7 @@ constexpr int F8_WAVES = 4;
 constexpr int F8_BR = 32 * F8_WAVES;       // query rows per workgroup
 constexpr int F8_BC = TILE_ROWS;           // keys per tile
 constexpr int F8_TILE_BYTES = TILE_ELEMS;  // 64 x 128 fp8
-constexpr float F8_RESCALE_SLACK = 8.0f;
+constexpr float F8_PSUM_LIMIT = 256.0f;   // largest partial row sum of P kept without a rescale
 
 // e with x * 2^-e in [128, 256) (0 for x == 0).
 __device__ __forceinline__ int pow2_exponent_8(float x) {
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
   const uint16_t* qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * HD;
   const int nkt = (p.Lk + F8_BC - 1) / F8_BC;
   const int64_t tile0 = (int64_t)(b * p.H + h) * nkt;
-  const int* kexp = kexp_all + tile0;
-  const int* vexp = vexp_all + tile0;
+  const_i32* kexp = const_ptr(kexp_all + tile0);   // scalar loads
+  const_i32* vexp = const_ptr(vexp_all + tile0);
 
   // ---- queries: rotate, one exponent per 64-row tile, fp8 in the B layout of 32x32x64
   const int i = qt * F8_BR + wave * 32 + col;
@@ -272,36 +272,49 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
         sv[kb][j] = x;
       }
     }
-    float mx = sv[0][0];
+    if (NEXT) scores(next_ks, e_k_next, s_nxt);
+    // P: fp32 for the row sum, e4m3 for PV (B operand: this lane's 32 keys in register order)
+    float psum;
+    i32x8 p8;
+    auto exps = [&]() {
+      float part[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[16];
+        part[kb] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
-    mx = xor32_max(mx);
-    if (POS_SCALE) mx *= c2;
-    if (__any(mx > m_run + F8_RESCALE_SLACK)) {
+        for (int j = 0; j < 16; ++j) {
+          if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
+          else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
+          part[kb] += pv[j];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          p8[4 * kb + w] = (int)pack_fp8x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
+      }
+      psum = part[0] + part[1];
+    };
+    exps();
+    // Lazy rescaling without a per-tile max: while every row's partial sum
+    // (32 of its P) stays <= F8_PSUM_LIMIT = 256, every P is <= 256, inside
+    // e4m3's range, and the tile is kept; otherwise (a larger score, the
+    // first tile with m = -inf, or a non-finite sum) m moves up to the exact
+    // tile max, O and l are rescaled and P is recomputed.
+    if (__any(!(psum <= F8_PSUM_LIMIT))) {
+      float mx = sv[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
+      mx = xor32_max(mx);
+      if (POS_SCALE) mx *= c2;
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m was -inf
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
-    }
-    if (NEXT) scores(next_ks, e_k_next, s_nxt);
-    // P: fp32 for the row sum, e4m3 for PV (B operand: this lane's 32 keys in register order)
-    float psum = 0.f;
-    i32x8 p8;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], c2, -m_run));
-        else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
-        psum += pv[j];
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) p8[4 * kb + w] = (int)pack_fp8x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
+      exps();
     }
     l_run += psum;
 #pragma unroll

@@ -170,6 +170,12 @@ __device__ __forceinline__ void tile_dma(uint16_t* lds_tile, const uint16_t* bas
   }
 }
 
+// Read-only arrays (not written during the kernel) read through the
+// constant address space: loads at uniform indices become scalar loads into
+// SGPRs instead of vector loads into VGPRs.
+using const_i32 = const __attribute__((address_space(4))) int;
+__device__ __forceinline__ const_i32* const_ptr(const int* p) { return (const_i32*)p; }
+
 // Wait for this wave's outstanding global (and LDS-DMA) loads.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
