@@ -18,11 +18,13 @@
 // matching the accumulator registers), so no LDS transpose read is needed.
 // The inverse rotation is fused into the dQ and dK stores.
 //
-//  * bwd_dkdv: workgroup = 128 keys (4 waves x 32, one wave per SIMD and up
-//    to 512 registers: K and V rows of the wave's keys stay in registers),
-//    loop over 64-query tiles staged as Q fp16 rows, (R q)^T, dO rows, dO^T.
-//    S = Q K^T and dP = dO V^T (lane owns key j); dV^T += dO^T P and
-//    dK~^T += (R q)^T dS take P / dS from the accumulators.
+//  * bwd_dv:   workgroup = 128 keys (4 waves x 32, two workgroups per CU),
+//    loop over 64-query tiles staged as Q fp16 rows and dO^T.  S = Q K^T
+//    (lane owns key j), dV^T += dO^T P with P from the accumulators.
+//  * bwd_dk:   workgroup = 256 keys (8 waves x 32, one workgroup per CU),
+//    query tiles staged as Q fp16 rows, dO rows and (R q)^T.  S = Q K^T,
+//    dP - Delta = dO V^T - Delta, dK~^T += (R q)^T dS.  (One kernel for both
+//    would hold K, V and both accumulators per wave: one wave per SIMD.)
 //  * bwd_dq:   workgroup = 256 queries (8 waves, two per SIMD), loop over
 //    64-key tiles staged as K fp16 rows, (R k)^T, V rows.  S^T = K Q^T,
 //    dP^T = V dO^T (lane owns query i), dQ~^T += (R k)^T dS^T.
@@ -36,7 +38,8 @@ namespace wanattn {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int DKDV_WAVES = 4;
+constexpr int DV_WAVES = 4;
+constexpr int DK_WAVES = 8;
 constexpr int DQ_WAVES = 8;
 
 // Store 4 consecutive head-dim elements [d0, d0+4) of token n (two rotary
@@ -65,25 +68,57 @@ __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* t
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup owns 128 keys (key tiles 2kb, 2kb+1); loop over 64-query tiles.
-// ---------------------------------------------------------------------------
+// dV and dK: one kernel each, so that either fits two waves per SIMD (a wave
+// holding the K and V rows of its keys and both accumulators would need the
+// whole register file: one wave per SIMD, nothing to hide LDS latency or
+// overlap the softmax with the MFMAs).  The scores are recomputed in both.
+// A wave owns 32 keys (lane owns key j); the loop runs over 64-query tiles.
 // KMASK: keys j >= k_lens[b] get P = 0 (cross-attention key padding).
+// ---------------------------------------------------------------------------
+
+// Per-wave key setup shared by both kernels.
+struct KeySide {
+  int b, h, nt, j;
+  int64_t tile0;     // first query tile of (b, h)
+  int64_t ktile0;    // first key tile of (b, h)
+  int ktile;         // key tile holding this wave's keys
+  bool key_ok, key_live, tile_ok;
+};
+
+template <int NW, bool KMASK>
+__device__ __forceinline__ KeySide key_side(const BwdParams& p, int wave, int col) {
+  KeySide k;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = logical % p.n_tiles;
+  const int bh = logical / p.n_tiles;
+  k.b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
+  k.h = bh / p.B;
+  k.nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;
+  const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;
+  k.tile0 = (int64_t)(k.b * p.H + k.h) * k.nt;
+  k.ktile0 = (int64_t)(k.b * p.H + k.h) * ntk;
+  // wave w: row 32*(w%2) + col of key tile (32 NW kb + 32 w) / 64
+  k.ktile = (NW / 2) * kb + (wave >> 1);
+  k.j = kb * 32 * NW + wave * 32 + col;
+  k.key_ok = k.j < p.Lk;
+  k.key_live = !KMASK || k.j < min(max(p.k_lens[k.b], 0), p.Lk);
+  k.tile_ok = k.ktile < ntk;
+  return k;
+}
+
+// dV_j = sum_i P_ij dO_i.  Workgroup = 128 keys (4 waves, two workgroups per
+// CU); query tiles staged as Q fp16 rows and dO^T.  S = Q K^T from the
+// wave's K rows in registers, dV^T += dO^T P with P from the accumulators.
 template <bool KMASK>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  // Two buffers of the four query-side tiles (Q fp16 rows, (Rq)^T, dO rows,
-  // dO^T) and of the row statistics, each a separate object named
-  // statically in the two-way unrolled loop: LDS reads of one buffer then do
-  // not wait for the copies in flight into the other.
+__global__ __launch_bounds__(64 * DV_WAVES, 2) void bwd_dv_kernel(BwdParams p) {
+  // Double-buffered tiles as separate objects, named statically in the
+  // two-way unrolled loop (LDS reads do not wait for copies in flight).
   __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds1[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t dot_lds0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t dot_lds1[TILE_ELEMS];
-  __shared__ float lse2_s0[TILE_ROWS], lse2_s1[TILE_ROWS];     // LSE * log2 e (+inf: no row)
-  __shared__ float delta_s0[TILE_ROWS], delta_s1[TILE_ROWS];
+  __shared__ __attribute__((aligned(16))) float lse2_s0[TILE_ROWS];   // LSE * log2 e (+inf: no row)
+  __shared__ __attribute__((aligned(16))) float lse2_s1[TILE_ROWS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,73 +126,206 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const KeySide ks = key_side<DV_WAVES, KMASK>(p, wv, col);
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = logical % p.n_tiles;
-  const int bh = logical / p.n_tiles;
-  const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
-  const int h = bh / p.B;
-  const int nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;     // query tiles
-  const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;    // key tiles
-  const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
-  const int64_t ktile0 = (int64_t)(b * p.H + h) * ntk;
+  bf16x8 kf[8];   // K fp16 (bit patterns): B operand of S
+  load_row_frags(kf, p.kf + (ks.ktile0 + (ks.tile_ok ? ks.ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half,
+                 ks.tile_ok);
+  const int e_k = ks.tile_ok ? p.kexp[ks.ktile0 + ks.ktile] : 0;
 
-  // This lane's key j: row 32*(wave%2) + col of key tile 2kb + wave/2.
-  const int ktile = 2 * kb + (wv >> 1);
-  const int j = kb * 128 + wave * 32 + col;
-  const bool key_ok = j < p.Lk;
-  const bool key_live = !KMASK || j < min(max(p.k_lens[b], 0), p.Lk);
-  const bool tile_ok = ktile < ntk;
-  bf16x8 kf[8], vf[8];   // K fp16 (bit patterns), V bf16: B operands of S and dP
-  load_row_frags(kf, p.kf + (ktile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
-  load_row_frags(vf, p.vr + (ktile0 + (tile_ok ? ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
-  const int e_k = tile_ok ? p.kexp[ktile0 + ktile] : 0;
-
-  f32x16 dk_acc[4], dv_acc[4];
+  f32x16 dv_acc[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    dk_acc[d] = f32x16{};
-    dv_acc[d] = f32x16{};
-  }
-  const float* lse_row = p.lse + ((int64_t)b * p.H + h) * p.Lq;
-  const float* delta_row = p.delta + ((int64_t)b * p.H + h) * p.Lq;
+  for (int d = 0; d < 4; ++d) dv_acc[d] = f32x16{};
+  const float* lse_row = p.lse + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
 
   uint32_t roff[4], toff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    roff[i] = rowtile_lane_off<DKDV_WAVES>(wv, i, lane);
-    toff[i] = ttile_lane_off<DKDV_WAVES>(wv, i, lane);
+    roff[i] = rowtile_lane_off<DV_WAVES>(wv, i, lane);
+    toff[i] = ttile_lane_off<DV_WAVES>(wv, i, lane);
   }
-  const uint32_t bytes = (uint32_t)nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
-  const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + tile0 * TILE_ELEMS, bytes);
-  const __amdgpu_buffer_rsrc_t qtr = tile_rsrc(p.qt + tile0 * TILE_ELEMS, bytes);
-  const __amdgpu_buffer_rsrc_t dor = tile_rsrc(p.dor + tile0 * TILE_ELEMS, bytes);
-  const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + tile0 * TILE_ELEMS, bytes);
-  const_i32* qexp = const_ptr(p.qexp + tile0);   // scalar loads
+  const uint32_t bytes = (uint32_t)ks.nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+  const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + ks.tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + ks.tile0 * TILE_ELEMS, bytes);
+  const_i32* qexp = const_ptr(p.qexp + ks.tile0);   // scalar loads
 
   struct Buf {
     uint16_t* q;
-    uint16_t* qt;
-    uint16_t* dO;
     uint16_t* dOt;
     float* lse2;
-    float* delta;
   };
-  const Buf buf0{q_lds0, qt_lds0, do_lds0, dot_lds0, lse2_s0, delta_s0};
-  const Buf buf1{q_lds1, qt_lds1, do_lds1, dot_lds1, lse2_s1, delta_s1};
-
+  const Buf buf0{q_lds0, dot_lds0, lse2_s0};
+  const Buf buf1{q_lds1, dot_lds1, lse2_s1};
   auto stage = [&](const Buf& dst, int t) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      buf_dma16(qfr, roff[i], soff, tile_lds_block<DKDV_WAVES>(dst.q, wv, i));
-      buf_dma16(qtr, toff[i], soff, tile_lds_block<DKDV_WAVES>(dst.qt, wv, i));
-      buf_dma16(dor, roff[i], soff, tile_lds_block<DKDV_WAVES>(dst.dO, wv, i));
-      buf_dma16(dotr, toff[i], soff, tile_lds_block<DKDV_WAVES>(dst.dOt, wv, i));
+      buf_dma16(qfr, roff[i], soff, tile_lds_block<DV_WAVES>(dst.q, wv, i));
+      buf_dma16(dotr, toff[i], soff, tile_lds_block<DV_WAVES>(dst.dOt, wv, i));
+    }
+  };
+  // LSE of query tile t: threads 0..63, into a register, published to LDS
+  // once loaded (rows past Lq, and rows with no valid key, get +inf: P = 0).
+  auto load_stats = [&](int t) {
+    float x = -INFINITY;
+    if (tid < TILE_ROWS) {
+      const int i = t * TILE_ROWS + tid;
+      if (i < p.Lq) x = lse_row[i];
+    }
+    return x;
+  };
+  auto store_stats = [&](const Buf& dst, float x) {
+    if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
+  };
+
+  int e_q;
+  {
+    const float st = load_stats(0);
+    stage(buf0, 0);
+    e_q = qexp[0];
+    wait_vmem();
+    store_stats(buf0, st);
+  }
+  __syncthreads();
+
+  auto iteration = [&](auto parity, int t) {
+    constexpr int P = decltype(parity)::value;
+    const Buf& cur = P ? buf1 : buf0;
+    const Buf& nxt = P ? buf0 : buf1;
+    const bool has_next = t + 1 < ks.nt;
+    int e_q_next = 0;
+    float st = 0.f;
+    if (has_next) {
+      st = load_stats(t + 1);
+      stage(nxt, t + 1);
+      e_q_next = qexp[t + 1];
+    }
+    const float g = ldexpf(p.scale_log2, e_q + e_k);
+    bf16x8 pf[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s_acc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
+      float pv[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
+          if (KMASK && !ks.key_live) pe = 0.f;
+          pv[4 * m + e] = pe;
+        }
+      }
+      pf[2 * qb] = pack_acc8(pv);
+      pf[2 * qb + 1] = pack_acc8(pv + 8);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int qg = 0; qg < 4; ++qg) dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
+    }
+    if (has_next) {
+      wait_vmem();
+      store_stats(nxt, st);
+    }
+    __syncthreads();
+    e_q = e_q_next;
+  };
+  int t = 0;
+  for (; t + 1 < ks.nt; t += 2) {
+    iteration(std::integral_constant<int, 0>{}, t);
+    iteration(std::integral_constant<int, 1>{}, t + 1);
+  }
+  if (t < ks.nt) iteration(std::integral_constant<int, 0>{}, t);
+
+  if (ks.key_ok) {
+    uint16_t* dvrow = p.dv + ((int64_t)ks.b * p.Lk * p.H + ks.h) * HD + (int64_t)ks.j * p.H * HD;
+    RopeDev none = p.rope;
+    none.table = nullptr;
+    const TokenPos pos{0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        store_grad4(dvrow, none, pos, d * 32 + 8 * jq + 4 * half, dv_acc[d][4 * jq], dv_acc[d][4 * jq + 1],
+                    dv_acc[d][4 * jq + 2], dv_acc[d][4 * jq + 3]);
+    }
+  }
+}
+
+// dk~_j = scale sum_i dS_ij q~_i, dS_ij = P_ij (<dO_i, v_j> - Delta_i).
+// Workgroup = 256 keys (8 waves, one workgroup per CU); query tiles staged
+// as Q fp16 rows, dO rows and (R q)^T.  S = Q K^T and dP - Delta = dO V^T -
+// Delta (the accumulator starts at -Delta of its rows) from the wave's K
+// and V rows in registers; dK~^T += (R q)^T dS with dS from the accumulators.
+template <bool KMASK>
+__global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) float lse2_s0[TILE_ROWS];   // LSE * log2 e (+inf: no row)
+  __shared__ __attribute__((aligned(16))) float lse2_s1[TILE_ROWS];
+  __shared__ __attribute__((aligned(16))) float ndelta_s0[TILE_ROWS];   // -Delta
+  __shared__ __attribute__((aligned(16))) float ndelta_s1[TILE_ROWS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const KeySide ks = key_side<DK_WAVES, KMASK>(p, wv, col);
+
+  bf16x8 kf[8], vf[8];   // K fp16 (bit patterns), V bf16: B operands of S and dP
+  const int64_t ktile = ks.ktile0 + (ks.tile_ok ? ks.ktile : 0);
+  load_row_frags(kf, p.kf + ktile * TILE_ELEMS, 32 * (wave & 1) + col, half, ks.tile_ok);
+  load_row_frags(vf, p.vr + ktile * TILE_ELEMS, 32 * (wave & 1) + col, half, ks.tile_ok);
+  const int e_k = ks.tile_ok ? p.kexp[ks.ktile0 + ks.ktile] : 0;
+
+  f32x16 dk_acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dk_acc[d] = f32x16{};
+  const float* lse_row = p.lse + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
+  const float* delta_row = p.delta + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
+
+  uint32_t roff[2], toff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    roff[i] = rowtile_lane_off<DK_WAVES>(wv, i, lane);
+    toff[i] = ttile_lane_off<DK_WAVES>(wv, i, lane);
+  }
+  const uint32_t bytes = (uint32_t)ks.nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+  const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + ks.tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t dor = tile_rsrc(p.dor + ks.tile0 * TILE_ELEMS, bytes);
+  const __amdgpu_buffer_rsrc_t qtr = tile_rsrc(p.qt + ks.tile0 * TILE_ELEMS, bytes);
+  const_i32* qexp = const_ptr(p.qexp + ks.tile0);   // scalar loads
+
+  struct Buf {
+    uint16_t* q;
+    uint16_t* dO;
+    uint16_t* qt;
+    float* lse2;
+    float* ndelta;
+  };
+  const Buf buf0{q_lds0, do_lds0, qt_lds0, lse2_s0, ndelta_s0};
+  const Buf buf1{q_lds1, do_lds1, qt_lds1, lse2_s1, ndelta_s1};
+  auto stage = [&](const Buf& dst, int t) {
+    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      buf_dma16(qfr, roff[i], soff, tile_lds_block<DK_WAVES>(dst.q, wv, i));
+      buf_dma16(dor, roff[i], soff, tile_lds_block<DK_WAVES>(dst.dO, wv, i));
+      buf_dma16(qtr, toff[i], soff, tile_lds_block<DK_WAVES>(dst.qt, wv, i));
     }
   };
   // Row statistics of query tile t: threads 0..63 read LSE, 64..127 Delta,
-  // into a register (published to LDS by store_stats once loaded).
+  // into a register, published to LDS once loaded.
   auto load_stats = [&](int t) {
     float x = 0.f;
     if (tid < TILE_ROWS) {
@@ -172,11 +340,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto store_stats = [&](const Buf& dst, float x) {
     // rows past Lq, and rows with no valid key (LSE = -inf), contribute nothing
     if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
-    else if (tid < 2 * TILE_ROWS) dst.delta[tid - TILE_ROWS] = x;
+    else if (tid < 2 * TILE_ROWS) dst.ndelta[tid - TILE_ROWS] = -x;
   };
 
-  // A tile's exponent and statistics are loaded with its copies, so the
-  // wait that ends the previous tile covers them.
   int e_q;
   {
     const float st = load_stats(0);
@@ -187,13 +353,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // Query tile t with parity P = t & 1: tile t in buffer P, tile t+1 copied
-  // into buffer 1-P.
   auto iteration = [&](auto parity, int t) {
     constexpr int P = decltype(parity)::value;
     const Buf& cur = P ? buf1 : buf0;
     const Buf& nxt = P ? buf0 : buf1;
-    const bool has_next = t + 1 < nt;
+    const bool has_next = t + 1 < ks.nt;
     int e_q_next = 0;
     float st = 0.f;
     if (has_next) {
@@ -202,39 +366,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       e_q_next = qexp[t + 1];
     }
     const float g = ldexpf(p.scale_log2, e_q + e_k);
-
-    bf16x8 pf[4], dsf[4];
+    bf16x8 dsf[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+      // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
+      f32x16 s_acc = f32x16{}, dp_acc;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(cur.ndelta + qb * 32 + 8 * m + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp_acc[4 * m + e] = nd[e];
+      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
         dp_acc = mfma32(lds_row_frag(cur.dO, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
       }
-      float pv[16], dsv[16];
+      float dsv[16];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int r = qb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);   // query row in the tile
-        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -cur.lse2[r]));
-        if (KMASK && !key_live) pe = 0.f;
-        pv[jj] = pe;
-        dsv[jj] = pe * (dp_acc[jj] - cur.delta[r]);
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
+          if (KMASK && !ks.key_live) pe = 0.f;
+          dsv[4 * m + e] = pe * dp_acc[4 * m + e];
+        }
       }
-      pf[2 * qb] = pack_acc8(pv);
-      pf[2 * qb + 1] = pack_acc8(pv + 8);
       dsf[2 * qb] = pack_acc8(dsv);
       dsf[2 * qb + 1] = pack_acc8(dsv + 8);
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int qg = 0; qg < 4; ++qg) {
-        dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
-        dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
-      }
+      for (int qg = 0; qg < 4; ++qg) dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
     }
-
     if (has_next) {
       wait_vmem();
       store_stats(nxt, st);
@@ -243,31 +409,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     e_q = e_q_next;
   };
   int t = 0;
-  for (; t + 1 < nt; t += 2) {
+  for (; t + 1 < ks.nt; t += 2) {
     iteration(std::integral_constant<int, 0>{}, t);
     iteration(std::integral_constant<int, 1>{}, t + 1);
   }
-  if (t < nt) iteration(std::integral_constant<int, 0>{}, t);
+  if (t < ks.nt) iteration(std::integral_constant<int, 0>{}, t);
 
-  if (key_ok) {
+  if (ks.key_ok) {
     TokenPos pos{0, 0, 0};
-    if (p.rope.table != nullptr) pos = token_pos(p.rope, j);
-    const int64_t rs = (int64_t)p.H * HD;
-    const int64_t head_off = ((int64_t)b * p.Lk * p.H + h) * HD;
-    uint16_t* dkrow = p.dk + head_off + (int64_t)j * rs;
-    uint16_t* dvrow = p.dv + head_off + (int64_t)j * rs;
-    RopeDev none = p.rope;
-    none.table = nullptr;
+    if (p.rope.table != nullptr) pos = token_pos(p.rope, ks.j);
+    uint16_t* dkrow = p.dk + ((int64_t)ks.b * p.Lk * p.H + ks.h) * HD + (int64_t)ks.j * p.H * HD;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int d0 = d * 32 + 8 * jq + 4 * half;
-        store_grad4(dkrow, p.rope, pos, d0, dk_acc[d][4 * jq] * p.scale, dk_acc[d][4 * jq + 1] * p.scale,
-                    dk_acc[d][4 * jq + 2] * p.scale, dk_acc[d][4 * jq + 3] * p.scale);
-        store_grad4(dvrow, none, pos, d0, dv_acc[d][4 * jq], dv_acc[d][4 * jq + 1], dv_acc[d][4 * jq + 2],
-                    dv_acc[d][4 * jq + 3]);
-      }
+      for (int jq = 0; jq < 4; ++jq)
+        store_grad4(dkrow, p.rope, pos, d * 32 + 8 * jq + 4 * half, dk_acc[d][4 * jq] * p.scale,
+                    dk_acc[d][4 * jq + 1] * p.scale, dk_acc[d][4 * jq + 2] * p.scale, dk_acc[d][4 * jq + 3] * p.scale);
     }
   }
 }
@@ -427,13 +584,20 @@ bool tiles_addressable(int L) {
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
   if (!tiles_addressable(p.Lq) || !tiles_addressable(p.Lk)) return hipErrorInvalidValue;
   BwdParams q = p;
-  q.n_tiles = (p.Lk + 127) / 128;
-  const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
+  q.n_tiles = (p.Lk + 32 * DV_WAVES - 1) / (32 * DV_WAVES);
+  int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   if (p.k_lens != nullptr)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3((unsigned)total), dim3(64 * DKDV_WAVES), 0, stream, q);
+    hipLaunchKernelGGL(bwd_dv_kernel<true>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
   else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3((unsigned)total), dim3(64 * DKDV_WAVES), 0, stream, q);
+    hipLaunchKernelGGL(bwd_dv_kernel<false>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
+  q.n_tiles = (p.Lk + 32 * DK_WAVES - 1) / (32 * DK_WAVES);
+  total = (int64_t)q.n_tiles * p.H * p.B;
+  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.k_lens != nullptr)
+    hipLaunchKernelGGL(bwd_dk_kernel<true>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);
+  else
+    hipLaunchKernelGGL(bwd_dk_kernel<false>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);
   return hipGetLastError();
 }
 
