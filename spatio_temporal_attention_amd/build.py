@@ -16,8 +16,12 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libwanattn.so")
 
-SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "merge.hip",
-           "validate.cpp"]
+SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
+           "merge.hip", "validate.cpp"]
+# Per-file compiler options.  The self-attention forward's products phase
+# needs the iterative ILP machine scheduler to keep LDS reads ahead of its
+# MFMAs (the default one reads each fragment right before its use there).
+EXTRA_FLAGS = {"attn_fwd_pp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = "gfx950"
 
 
@@ -33,7 +37,7 @@ def _flags(src: str):
     if src.endswith(".hip"):
         # Packed fp32 VALU ops are disabled: the kernels are written for scalar fp32.
         return common + [f"--offload-arch={ARCH}", "-x", "hip",
-                         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+                         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + EXTRA_FLAGS.get(src, [])
     return common
 
 

@@ -1,0 +1,394 @@
+// Self-attention forward for gfx950 over the tiles the K/V prep pass writes
+// (kv_prep.hip): full spatio-temporal attention with 3D RoPE, the rotation
+// applied to the queries on load (keys arrive rotated).
+//
+// Computes, per (batch b, head h, query i), over the valid keys j < n_keys:
+//   s_ij = scale <q~_i, k~_j>,  O_i = sum_j softmax_j(s_ij) v_j,  LSE_i = ln sum_j exp(s_ij)
+// -- full spatio-temporal attention over latent patches ("Wan Team, Alibaba
+// (2025)", Key takeaways, Backbone) with positions entering through 3D RoPE
+// (Wan2.1 reading notes, 2. Model Design, DiT block paragraph).  The same
+// kernel serves variable lengths (q_lens, k_lens) and key/query shards at
+// token offsets (q_pos0, k_pos0: RoPE at global positions).
+//
+// Design (one workgroup = 8 waves = 256 query rows of one (b, h), one
+// workgroup per CU, two waves per SIMD):
+//  * each wave keeps its 32 rotated query rows in registers as the B operand
+//    of S^T = K Q^T (MFMA 32x32x16), so every lane owns one query row;
+//  * with RoPE the score product runs in fp16 (3 more mantissa bits than
+//    bf16, same MFMA rate).  Each 64-row tile of rotated queries is scaled by
+//    2^-e_q so that its largest |element| lies in [2^14, 2^15) and rounded to
+//    fp16; the key prep pass does the same per 64-key tile (exponent e_t);
+//    the softmax applies s = scale * 2^(e_q + e_t) * S.  The backward's prep
+//    passes reproduce these fp16 operands bit for bit.  (Rounding the rotated
+//    query to bf16 instead would move LSE by up to ~1.2e-3 at 720p: a query's
+//    rounding error shifts all its scores coherently.)  Without RoPE the bf16
+//    inputs are used as given;
+//  * K tiles (64 keys, row-major) and V^T tiles (token order matching the
+//    accumulator registers) go global -> LDS by buffer_load ... lds,
+//    double-buffered; O^T += V^T P^T takes P straight from the S^T
+//    accumulators (bf16, RNE) with plain 16-byte LDS reads of V^T;
+//  * online softmax in fp32, log2 domain, with lazy rescaling that takes no
+//    per-tile max (m moves only when a row's partial sum of P would exceed
+//    2^16);
+//  * ping-pong: each wave alternates a softmax phase (VALU) and a products
+//    phase (MFMA: O += P(t) V(t), then the scores of tile t+1); waves 4..7
+//    run one phase behind waves 0..3 and all eight meet at a barrier after
+//    every phase, so on each SIMD (waves w and w + 4) one wave feeds the
+//    matrix cores while the other runs its softmax;
+//  * workgroups are ordered head-major and XCD-aware (batch item innermost),
+//    so the resident workgroups of one XCD walk the same head's K/V tiles
+//    through its L2.
+// Built with the iterative ILP machine scheduler (build flags of this file):
+// with the default one the products phase reads each LDS fragment just before
+// its MFMA.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace wanattn {
+
+namespace {
+
+constexpr int FWD_BC = TILE_ROWS;         // keys per tile
+constexpr float PSUM_LIMIT = 65536.0f;    // largest partial row sum of P kept without a rescale
+
+// Phase schedule:
+//   barrier k:  waves 0..3 have finished their phase k, waves 4..7 phase k-1
+//   (phase 2t = softmax(t), phase 2t+1 = products(t)).
+// K(t+1) and V(t) are read during products(t) (between barriers 2t and 2t+2
+// over both groups).  The early waves alone copy the tiles: K(t+2) and
+// V(t+1), into the buffers K(t) and V(t-1) leave, are issued after barrier
+// 2t and waited for before barrier 2t+1.  Both groups run the same code; the
+// late waves add a barrier before their first phase, the early ones one
+// after their last.
+
+constexpr int PP_WAVES = 8;
+constexpr int PP_BR = 32 * PP_WAVES;   // query rows per workgroup
+
+template <bool POS_SCALE, bool F16>
+// Two waves per SIMD by design (one workgroup per CU); without the explicit
+// target the compiler aims for four (the LDS would allow two workgroups) and
+// schedules for register pressure instead of latency.
+__global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(
+    FwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[TILE_ELEMS];
+  __shared__ float qmax_s[PP_WAVES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool late = wv >= PP_WAVES / 2;   // waves 4..7: one phase behind
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = logical % p.n_qtiles;
+  const int bh = logical / p.n_qtiles;
+  const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
+  const int h = bh / p.B;
+
+  int n_keys = p.Lk;
+  if (p.k_lens != nullptr) n_keys = min(max(p.k_lens[b], 0), p.Lk);
+  const int64_t q_row_stride = (int64_t)p.H * HD;
+  const uint16_t* qbase = p.q + ((int64_t)b * p.Lq * p.H + h) * HD;
+  const int nkt = (p.Lk + FWD_BC - 1) / FWD_BC;
+  const int64_t tile0 = (int64_t)(b * p.H + h) * nkt;
+
+  const int i = qt * PP_BR + wave * 32 + col;
+  int n_q = p.Lq;
+  if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
+  const bool row_ok = i < n_q;
+  bf16x8 qf[8];
+  float g_q = p.scale_log2;
+  {
+    TokenPos pos{0, 0, 0};
+    if (p.rope.table != nullptr && row_ok) pos = token_pos(p.rope, p.q_pos0 + i);
+    if (F16) {
+      float y[8][8];
+      float mq = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 2 * s + half;
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (row_ok) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float y0 = bf16_lo(x[t]);
+          float y1 = bf16_hi(x[t]);
+          if (row_ok) rope_rotate(y0, y1, rope_cs(p.rope, pos, 4 * c + t), false);
+          y[s][2 * t] = y0;
+          y[s][2 * t + 1] = y1;
+          mq = fmaxf(mq, fmaxf(fabsf(y0), fabsf(y1)));
+        }
+      }
+      // One exponent per 64-row query tile (waves 2u and 2u+1).
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mq = fmaxf(mq, __shfl_xor(mq, o));
+      if (lane == 0) qmax_s[wave] = mq;
+      __syncthreads();
+      const int e_q = pow2_exponent_15(fmaxf(qmax_s[wave & ~1], qmax_s[wave | 1]));
+      g_q = ldexpf(p.scale_log2, e_q);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = pack_f16(ldexpf(y[s][2 * t], -e_q), ldexpf(y[s][2 * t + 1], -e_q));
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        const int c = 2 * s + half;
+        if (row_ok) {
+          x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)i * q_row_stride + c * 8);
+          if (p.rope.table != nullptr) x = rope_chunk(p.rope, pos, c, x, false);
+        }
+        qf[s] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  }
+
+  f32x16 o_acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o_acc[d] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const_i32* kexp = F16 ? const_ptr(p.kexp + tile0) : nullptr;   // scalar loads
+  const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
+
+  if (n_tiles > 0) {
+    // Copies by the 4 early waves (4 x 1 KB per tile and wave); the prologue
+    // uses the same offsets.
+    constexpr int CW = PP_WAVES / 2;
+    const int cw = late ? wv - CW : wv;
+    uint32_t koff[4], voff[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      koff[c] = rowtile_lane_off<CW>(cw, c, lane);
+      voff[c] = ttile_lane_off<CW>(cw, c, lane);
+    }
+    const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(p.kt + tile0 * TILE_ELEMS, bytes);
+    const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(p.vt + tile0 * TILE_ELEMS, bytes);
+    auto stage_k = [&](uint16_t* dst, int t) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        buf_dma16(krs, koff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<CW>(dst, cw, c));
+    };
+    auto stage_v = [&](uint16_t* dst, int t) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        buf_dma16(vrs, voff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<CW>(dst, cw, c));
+    };
+
+    f32x16 s_acc[2];
+    auto scores = [&](const uint16_t* ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s_acc[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 a = lds_row_frag(ks, kb * 32 + col, 2 * s + half);
+          s_acc[kb] = F16 ? mfma32_f16(a, qf[s], s_acc[kb]) : mfma32(a, qf[s], s_acc[kb]);
+        }
+      }
+    };
+
+    // Softmax of tile t (VALU phase): P into pf.  MASK: the partial last tile.
+    bf16x8 pf[4];
+    auto softmax = [&](auto mask_tag, int t, int e_t) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const float g = F16 ? ldexpf(g_q, e_t) : g_q;
+      float sv[2][16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float x = POS_SCALE ? s_acc[kb][j] : s_acc[kb][j] * g;
+          if (MASK) {
+            const int key = t * FWD_BC + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (key >= n_keys) x = -INFINITY;
+          }
+          sv[kb][j] = x;
+        }
+      }
+      float psum;
+      auto exps = [&]() {
+        float part[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float pv[16];
+          part[kb] = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (POS_SCALE) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[kb][j], g, -m_run));
+            else pv[j] = __builtin_amdgcn_exp2f(sv[kb][j] - m_run);
+            part[kb] += pv[j];
+          }
+          pf[2 * kb] = pack_acc8(pv);
+          pf[2 * kb + 1] = pack_acc8(pv + 8);
+        }
+        psum = part[0] + part[1];
+      };
+      exps();
+      // Lazy rescaling without a per-tile max: while every row's partial
+      // sum (32 of its P) stays <= PSUM_LIMIT, so does every P, and the tile
+      // is kept (scores up to m + 11 in log2 units always are); otherwise (a
+      // larger score, the first tile with m = -inf, a non-finite sum) m moves
+      // up to the exact tile max, O and l are rescaled and P is recomputed.
+      // Exact either way: O / l and LSE = m + log2 l use the m applied.
+      if (__any(!(psum <= PSUM_LIMIT))) {
+        float mx = sv[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sv[kb][j]);
+        mx = xor32_max(mx);
+        if (POS_SCALE) mx *= g;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o_acc[d] *= alpha;
+        exps();
+      }
+      l_run += psum;
+    };
+
+    // O^T += V^T P^T (MFMA phase, first half).
+    auto pv_product = [&](const uint16_t* vs) {
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        bf16x8 a[2][4];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int kg = 0; kg < 4; ++kg) a[d][kg] = lds_vt_frag(vs, (2 * hd + d) * 32 + col, kg, half);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) o_acc[2 * hd + d] = mfma32(a[d][kg], pf[kg], o_acc[2 * hd + d]);
+      }
+    };
+
+    // Prologue: K(0), V(0), K(1) staged; S(0) by every wave.
+    if (!late) {
+      stage_k(k_lds0, 0);
+      stage_v(v_lds0, 0);
+      if (n_tiles > 1) stage_k(k_lds1, 1);
+    }
+    wait_vmem();
+    __syncthreads();
+    scores(k_lds0);
+    const int last = n_tiles - 1;
+    const bool partial = n_keys % FWD_BC != 0;
+    if (late) __syncthreads();   // the early waves run softmax(0) meanwhile
+
+    // Tile t with parity P = t & 1: K(t+1) in K buffer 1-P, V(t) in V buffer
+    // P; K(t+2) is copied into K buffer P, V(t+1) into V buffer 1-P.
+    auto tile = [&](auto parity, int t) {
+      constexpr int P = decltype(parity)::value;
+      uint16_t* const k_fill = P ? k_lds1 : k_lds0;
+      const uint16_t* const k_next = P ? k_lds0 : k_lds1;
+      const uint16_t* const v_cur = P ? v_lds1 : v_lds0;
+      uint16_t* const v_fill = P ? v_lds0 : v_lds1;
+      const int e_t = F16 ? kexp[t] : 0;
+      if constexpr (POS_SCALE) {
+        // The partial last tile: keys past n_keys get a score of -inf in
+        // place (exact under the positive factor), so one softmax serves
+        // every tile (a second, masked copy costs ~50 VGPRs).
+        if (partial && t == last) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int key = t * FWD_BC + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+              if (key >= n_keys) s_acc[kb][j] = -INFINITY;
+            }
+        }
+        softmax(std::false_type{}, t, e_t);
+      } else {
+        if (partial && t == last) softmax(std::true_type{}, t, e_t);
+        else softmax(std::false_type{}, t, e_t);
+      }
+      __syncthreads();   // barrier 2t (early waves), 2t+1 (late waves)
+      if (!late) {
+        if (t + 2 < n_tiles) stage_k(k_fill, t + 2);
+        if (t + 1 < n_tiles) stage_v(v_fill, t + 1);
+      }
+      pv_product(v_cur);
+      if (t < last) {
+        scores(k_next);
+        // Keep four fragment reads in flight ahead of the MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < 28; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        wait_vmem();
+        __syncthreads();   // barrier 2t+1 (early), 2t+2 (late)
+      }
+    };
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      tile(std::integral_constant<int, 0>{}, t);
+      tile(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (t < n_tiles) tile(std::integral_constant<int, 0>{}, t);
+    if (!late) __syncthreads();   // matches the late waves' barrier before their last products phase
+  }
+
+  const float l_tot = xor32_sum(l_run);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    uint16_t* orow = p.o + ((int64_t)b * p.Lq * p.H + h) * HD + (int64_t)i * q_row_stride;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        u32x2 w;
+        w[0] = pack_bf16(o_acc[d][4 * jq] * inv, o_acc[d][4 * jq + 1] * inv);
+        w[1] = pack_bf16(o_acc[d][4 * jq + 2] * inv, o_acc[d][4 * jq + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d * 32 + 8 * jq + 4 * half) = w;
+      }
+    }
+    if (p.lse != nullptr && half == 0) {
+      const float lse = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+      p.lse[((int64_t)b * p.H + h) * p.Lq + i] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
+  if (p.kt == nullptr || p.vt == nullptr) return hipErrorInvalidValue;
+  // The tiles of one (b, h) are addressed through a buffer resource of 32-bit extent.
+  if ((int64_t)((p.Lk + FWD_BC - 1) / FWD_BC) * (TILE_ELEMS * 2) > (int64_t)0xffffffff) return hipErrorInvalidValue;
+  const bool f16 = p.rope.table != nullptr;   // fp16 scores against the fp16 key tiles
+  if (f16 && p.kexp == nullptr) return hipErrorInvalidValue;
+  FwdParams r = p;
+  r.n_qtiles = (p.Lq + PP_BR - 1) / PP_BR;
+  const int64_t n = (int64_t)r.n_qtiles * p.H * p.B;
+  if (n <= 0 || n > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n), block(64 * PP_WAVES);
+  if (p.scale_log2 > 0.f) {
+    if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true>), grid, block, 0, stream, r);
+    else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false>), grid, block, 0, stream, r);
+  } else {
+    if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true>), grid, block, 0, stream, r);
+    else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false>), grid, block, 0, stream, r);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wanattn

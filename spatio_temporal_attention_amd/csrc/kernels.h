@@ -73,6 +73,9 @@ struct MergeParams {
 };
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
+// Self-attention over the prep pass's tiles (p.kt, p.vt, and p.kexp with RoPE); launch_attn_fwd
+// dispatches here when p.kt is set.
+hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream);
 // FP8 forward: K as e4m3 row tiles [64][128] and V as e4m3 V^T tiles [128][64]
 // (8 KB each, key order kappa), with int32 exponents per tile.
 hipError_t launch_kv8_tiles(const uint16_t* k, const uint16_t* v, uint8_t* k8, int* kexp, uint8_t* v8, int* vexp,
