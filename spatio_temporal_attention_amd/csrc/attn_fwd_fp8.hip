@@ -38,6 +38,15 @@ constexpr int F8_BC = TILE_ROWS;           // keys per tile
 constexpr int F8_TILE_BYTES = TILE_ELEMS;  // 64 x 128 fp8
 constexpr float F8_PSUM_LIMIT = 256.0f;   // largest partial row sum of P kept without a rescale
 
+// Four P values (each in [0, 256] on the path that uses them: see the
+// partial-sum check) to e4m3, RNE, without the clamp of pack_fp8x4: values
+// that could overflow (P = +inf or NaN while m = -inf) are recomputed before
+// the product reads them.
+__device__ __forceinline__ uint32_t pack_p8x4(float a, float b, float c, float d) {
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+}
+
 // e with x * 2^-e in [128, 256) (0 for x == 0).
 __device__ __forceinline__ int pow2_exponent_8(float x) {
   if (!(x > 0.f)) return 0;
@@ -289,8 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
           part[kb] += pv[j];
         }
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          p8[4 * kb + w] = (int)pack_fp8x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
+        for (int w = 0; w < 4; ++w) p8[4 * kb + w] = (int)pack_p8x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
       }
       psum = part[0] + part[1];
     };
