@@ -118,6 +118,8 @@ def test_self_fwd_tiny_workload():
     (1, (4, 8, 8), 2, False, 8.0),      # peaked softmax: exercises the running-max rescale
     (3, (1, 9, 15), 1, False, 3.0),     # B > 1, L = 135, peaked
     (2, (3, 7, 9), 2, True, 1.0),       # B > 1, L = 189 with RoPE
+    (1, (2, 13, 20), 2, True, 1.0),     # L = 520: three 256-row workgroups (the last with 8 rows), 9 key tiles
+    (1, (2, 16, 16), 1, True, 1.0),     # L = 512: two full workgroups, an even number of full key tiles
 ])
 def test_self_fwd_small(B, grid, H, rope_on, qmul):
     L = int(np.prod(grid))

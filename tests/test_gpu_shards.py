@@ -60,6 +60,26 @@ def test_varlen_matches_oracle_and_leaves_padding(rope_on):
         assert np.all(gl[b, :, n:] == 5.0), "LSE past the length was written"
 
 
+def test_varlen_with_empty_items():
+    """Items of length 0 (no key tile, no row) next to a full one: nothing of theirs is written."""
+    B, L, H = 3, 320, 2
+    lens = np.array([0, 320, 0], dtype=np.int32)
+    qb, kb, vb = _inputs(700, (B, L, H, 128))
+    table = wa.rope_table(GRID, ROPE)
+    o = torch.full((B, L, H, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, L), 5.0, dtype=torch.float32, device="cuda")
+    wa.self_fwd_varlen(to_dev(qb), to_dev(kb), to_dev(vb), torch.from_numpy(lens).cuda(), grid=GRID, table=table,
+                       rope=ROPE, scale=SCALE, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.self_fwd_varlen_ref(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                                        synth.bf16_bits_to_f64(vb), lens, SCALE, GRID, ROPE)
+    go, gl = bf16_to_f64(o), f32_to_np(lse)
+    check_close("O", go[1], ro[1])
+    check_lse("LSE", gl[1], rl[1])
+    for b in (0, 2):
+        assert np.all(go[b] == 7.0) and np.all(gl[b] == 5.0), f"item {b} (length 0) was written"
+
+
 @pytest.mark.parametrize("q_off,lq,k_off,lk", [(96, 120, 200, 120), (0, 64, 0, 320), (250, 70, 3, 61)])
 def test_partial_fwd_matches_oracle(q_off, lq, k_off, lk):
     H = 2
