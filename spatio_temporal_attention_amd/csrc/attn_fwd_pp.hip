@@ -57,12 +57,14 @@ constexpr float PSUM_LIMIT = 65536.0f;    // largest partial row sum of P kept w
 //   barrier k:  waves 0..3 have finished their phase k, waves 4..7 phase k-1
 //   (phase 2t = softmax(t), phase 2t+1 = products(t)).
 // K(t+1) and V(t) are read during products(t) (between barriers 2t and 2t+2
-// over both groups).  The early waves alone copy the tiles: K(t+2) and
-// V(t+1), into the buffers K(t) and V(t-1) leave, are issued after barrier
-// 2t and waited for before barrier 2t+1.  Both groups run the same code; the
-// late waves add a barrier before their first phase, the early ones one
-// after their last.
-
+// over both groups).  K(t+2) and V(t+1) go into the buffers K(t) and V(t-1)
+// leave, 1/8 of each tile per wave, all issued after barrier 2t: the early
+// waves at the start of their products phase, the late waves at the start
+// of their softmax phase (the shorter phase); each wave waits for its own
+// copies before the barrier that ends its products phase (2t+1 and 2t+2),
+// before anyone reads them (products(t+1), after barrier 2t+2).  Both groups
+// run the same code; the late waves add a barrier before their first phase,
+// the early ones one after their last.
 constexpr int PP_WAVES = 8;
 constexpr int PP_BR = 32 * PP_WAVES;   // query rows per workgroup
 
@@ -163,28 +165,25 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
 
   if (n_tiles > 0) {
-    // Copies by the 4 early waves (4 x 1 KB per tile and wave); the prologue
-    // uses the same offsets.
-    constexpr int CW = PP_WAVES / 2;
-    const int cw = late ? wv - CW : wv;
-    uint32_t koff[4], voff[4];
+    // Each wave copies 1/8 of every K and V tile (2 x 1 KB each).
+    uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      koff[c] = rowtile_lane_off<CW>(cw, c, lane);
-      voff[c] = ttile_lane_off<CW>(cw, c, lane);
+    for (int c = 0; c < 2; ++c) {
+      koff[c] = rowtile_lane_off<PP_WAVES>(wv, c, lane);
+      voff[c] = ttile_lane_off<PP_WAVES>(wv, c, lane);
     }
     const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(p.kt + tile0 * TILE_ELEMS, bytes);
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(p.vt + tile0 * TILE_ELEMS, bytes);
     auto stage_k = [&](uint16_t* dst, int t) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        buf_dma16(krs, koff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<CW>(dst, cw, c));
+      for (int c = 0; c < 2; ++c)
+        buf_dma16(krs, koff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<PP_WAVES>(dst, wv, c));
     };
     auto stage_v = [&](uint16_t* dst, int t) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        buf_dma16(vrs, voff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<CW>(dst, cw, c));
+      for (int c = 0; c < 2; ++c)
+        buf_dma16(vrs, voff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<PP_WAVES>(dst, wv, c));
     };
 
     f32x16 s_acc[2];
@@ -279,11 +278,10 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
     };
 
     // Prologue: K(0), V(0), K(1) staged; S(0) by every wave.
-    if (!late) {
-      stage_k(k_lds0, 0);
-      stage_v(v_lds0, 0);
-      if (n_tiles > 1) stage_k(k_lds1, 1);
-    }
+    stage_k(k_lds0, 0);
+    stage_v(v_lds0, 0);
+    if (n_tiles > 1) stage_k(k_lds1, 1);
+    int e_nxt = F16 ? kexp[0] : 0;   // exponent of the next tile to take its softmax
     wait_vmem();
     __syncthreads();
     scores(k_lds0);
@@ -299,7 +297,17 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
       const uint16_t* const k_next = P ? k_lds0 : k_lds1;
       const uint16_t* const v_cur = P ? v_lds1 : v_lds0;
       uint16_t* const v_fill = P ? v_lds0 : v_lds1;
-      const int e_t = F16 ? kexp[t] : 0;
+      // The late waves issue their copies in this softmax phase (after
+      // barrier 2t), the early ones in their products phase; each waits for
+      // its own before the barrier that ends its products phase.
+      if (late) {
+        if (t + 2 < n_tiles) stage_k(k_fill, t + 2);
+        if (t + 1 < n_tiles) stage_v(v_fill, t + 1);
+      }
+      // Tile t's exponent was loaded one tile earlier; load tile t+1's now
+      // (scalar load, needed after two barriers).
+      const int e_t = e_nxt;
+      if (F16 && t + 1 < n_tiles) e_nxt = kexp[t + 1];
       if constexpr (POS_SCALE) {
         // The partial last tile: keys past n_keys get a score of -inf in
         // place (exact under the positive factor), so one softmax serves
