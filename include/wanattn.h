@@ -173,7 +173,11 @@ int wanattn_self_fwd_fp8(const void* q, const void* k, const void* v, void* o, f
  * 64-token tiles of every (b, h): q and k (rotated with a table) in fp16 with
  * the forward's per-tile powers of two, their bf16 transposes, dout (rows and
  * transposed) and v, so that P is recomputed from exactly the operands the
- * forward multiplied.  Its contents on return are unspecified.
+ * forward multiplied; when few key blocks would leave the GPU idle (a short
+ * key side: fewer than 256 blocks of 256 keys over B and H), the dK/dV passes
+ * split the query range and the workspace also holds their fp32 partial sums
+ * (reduced in a fixed order: results stay deterministic).  Its contents on
+ * return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 
@@ -261,7 +265,10 @@ int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t
  * H, D] bf16.  k_lens: device int32 [B] (clamped to [0, Lk]) or NULL (all
  * valid).  The score product runs in fp16 on power-of-two-scaled 64-token
  * tiles, as in the self-attention backward.
- * Workspace (required, 16-byte aligned): wanattn_cross_bwd_workspace_bytes.
+ * Workspace (required, 16-byte aligned): wanattn_cross_bwd_workspace_bytes
+ * (the self-attention backward's layout over Lq query and Lk key tokens,
+ * including the partial sums of a split query range: at the 720p text shape,
+ * B = 1, Lq = 75,600, Lk = 512, H = 40, the query range is split 7 ways).
  * ------------------------------------------------------------------------- */
 size_t wanattn_cross_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int D);
 

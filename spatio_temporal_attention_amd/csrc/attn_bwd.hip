@@ -28,6 +28,7 @@
 //  * bwd_dq:   workgroup = 256 queries (8 waves, two per SIMD), loop over
 //    64-key tiles staged as K fp16 rows, (R k)^T, V rows.  S^T = K Q^T,
 //    dP^T = V dO^T (lane owns query i), dQ~^T += (R k)^T dS^T.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -79,6 +80,7 @@ __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* t
 // Per-wave key setup shared by both kernels.
 struct KeySide {
   int b, h, nt, j;
+  int split, t0, t1;   // this workgroup's share [t0, t1) of the query tiles
   int64_t tile0;     // first query tile of (b, h)
   int64_t ktile0;    // first key tile of (b, h)
   int ktile;         // key tile holding this wave's keys
@@ -90,10 +92,15 @@ __device__ __forceinline__ KeySide key_side(const BwdParams& p, int wave, int co
   KeySide k;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = logical % p.n_tiles;
-  const int bh = logical / p.n_tiles;
+  const int rest = logical / p.n_tiles;
+  k.split = rest % p.q_split;
+  const int bh = rest / p.q_split;
   k.b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
   k.h = bh / p.B;
   k.nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;
+  const int chunk = (k.nt + p.q_split - 1) / p.q_split;
+  k.t0 = k.split * chunk;
+  k.t1 = min(k.nt, k.t0 + chunk);
   const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;
   k.tile0 = (int64_t)(k.b * p.H + k.h) * k.nt;
   k.ktile0 = (int64_t)(k.b * p.H + k.h) * ntk;
@@ -178,70 +185,84 @@ __global__ __launch_bounds__(64 * DV_WAVES, 2) void bwd_dv_kernel(BwdParams p) {
     if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
   };
 
-  int e_q;
-  {
-    const float st = load_stats(0);
-    stage(buf0, 0);
-    e_q = qexp[0];
-    wait_vmem();
-    store_stats(buf0, st);
-  }
-  __syncthreads();
+  // A query split can be empty (rounding of the split size): it writes zero partials.
+  if (ks.t0 < ks.t1) {
+    int e_q;
+    {
+      const float st = load_stats(ks.t0);
+      stage(buf0, ks.t0);
+      e_q = qexp[ks.t0];
+      wait_vmem();
+      store_stats(buf0, st);
+    }
+    __syncthreads();
 
-  auto iteration = [&](auto parity, int t) {
-    constexpr int P = decltype(parity)::value;
-    const Buf& cur = P ? buf1 : buf0;
-    const Buf& nxt = P ? buf0 : buf1;
-    const bool has_next = t + 1 < ks.nt;
-    int e_q_next = 0;
-    float st = 0.f;
-    if (has_next) {
-      st = load_stats(t + 1);
-      stage(nxt, t + 1);
-      e_q_next = qexp[t + 1];
-    }
-    const float g = ldexpf(p.scale_log2, e_q + e_k);
-    bf16x8 pf[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s_acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-      float pv[16];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
-          if (KMASK && !ks.key_live) pe = 0.f;
-          pv[4 * m + e] = pe;
-        }
+    auto iteration = [&](auto parity, int t) {
+      constexpr int P = decltype(parity)::value;
+      const Buf& cur = P ? buf1 : buf0;
+      const Buf& nxt = P ? buf0 : buf1;
+      const bool has_next = t + 1 < ks.t1;
+      int e_q_next = 0;
+      float st = 0.f;
+      if (has_next) {
+        st = load_stats(t + 1);
+        stage(nxt, t + 1);
+        e_q_next = qexp[t + 1];
       }
-      pf[2 * qb] = pack_acc8(pv);
-      pf[2 * qb + 1] = pack_acc8(pv + 8);
+      const float g = ldexpf(p.scale_log2, e_q + e_k);
+      bf16x8 pf[4];
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s_acc = f32x16{};
+  #pragma unroll
+        for (int s = 0; s < 8; ++s) s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
+        float pv[16];
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
+            if (KMASK && !ks.key_live) pe = 0.f;
+            pv[4 * m + e] = pe;
+          }
+        }
+        pf[2 * qb] = pack_acc8(pv);
+        pf[2 * qb + 1] = pack_acc8(pv + 8);
+      }
+  #pragma unroll
+      for (int d = 0; d < 4; ++d) {
+  #pragma unroll
+        for (int qg = 0; qg < 4; ++qg) dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
+      }
+      if (has_next) {
+        wait_vmem();
+        store_stats(nxt, st);
+      }
+      __syncthreads();
+      e_q = e_q_next;
+    };
+    int t = ks.t0;
+    for (; t + 1 < ks.t1; t += 2) {
+      iteration(std::integral_constant<int, 0>{}, t);
+      iteration(std::integral_constant<int, 1>{}, t + 1);
     }
+    if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
+  }
+
+  if (ks.key_ok && p.q_split > 1) {
+    // fp32 partial over this split's query tiles, summed by bwd_kv_reduce_kernel
+    const int64_t part = (int64_t)p.q_split * p.B * p.H * p.Lk * HD;   // dV follows dK~
+    float* row = p.part + part + ((((int64_t)ks.split * p.B + ks.b) * p.H + ks.h) * p.Lk + ks.j) * HD;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int qg = 0; qg < 4; ++qg) dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<f32x4*>(row + d * 32 + 8 * jq + 4 * half) =
+            f32x4{dv_acc[d][4 * jq], dv_acc[d][4 * jq + 1], dv_acc[d][4 * jq + 2], dv_acc[d][4 * jq + 3]};
     }
-    if (has_next) {
-      wait_vmem();
-      store_stats(nxt, st);
-    }
-    __syncthreads();
-    e_q = e_q_next;
-  };
-  int t = 0;
-  for (; t + 1 < ks.nt; t += 2) {
-    iteration(std::integral_constant<int, 0>{}, t);
-    iteration(std::integral_constant<int, 1>{}, t + 1);
-  }
-  if (t < ks.nt) iteration(std::integral_constant<int, 0>{}, t);
-
-  if (ks.key_ok) {
+  } else if (ks.key_ok) {
     uint16_t* dvrow = p.dv + ((int64_t)ks.b * p.Lk * p.H + ks.h) * HD + (int64_t)ks.j * p.H * HD;
     RopeDev none = p.rope;
     none.table = nullptr;
@@ -343,79 +364,92 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
     else if (tid < 2 * TILE_ROWS) dst.ndelta[tid - TILE_ROWS] = -x;
   };
 
-  int e_q;
-  {
-    const float st = load_stats(0);
-    stage(buf0, 0);
-    e_q = qexp[0];
-    wait_vmem();
-    store_stats(buf0, st);
-  }
-  __syncthreads();
+  // A query split can be empty (rounding of the split size): it writes zero partials.
+  if (ks.t0 < ks.t1) {
+    int e_q;
+    {
+      const float st = load_stats(ks.t0);
+      stage(buf0, ks.t0);
+      e_q = qexp[ks.t0];
+      wait_vmem();
+      store_stats(buf0, st);
+    }
+    __syncthreads();
 
-  auto iteration = [&](auto parity, int t) {
-    constexpr int P = decltype(parity)::value;
-    const Buf& cur = P ? buf1 : buf0;
-    const Buf& nxt = P ? buf0 : buf1;
-    const bool has_next = t + 1 < ks.nt;
-    int e_q_next = 0;
-    float st = 0.f;
-    if (has_next) {
-      st = load_stats(t + 1);
-      stage(nxt, t + 1);
-      e_q_next = qexp[t + 1];
-    }
-    const float g = ldexpf(p.scale_log2, e_q + e_k);
-    bf16x8 dsf[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
-      f32x16 s_acc = f32x16{}, dp_acc;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 nd = *reinterpret_cast<const f32x4*>(cur.ndelta + qb * 32 + 8 * m + 4 * half);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dp_acc[4 * m + e] = nd[e];
+    auto iteration = [&](auto parity, int t) {
+      constexpr int P = decltype(parity)::value;
+      const Buf& cur = P ? buf1 : buf0;
+      const Buf& nxt = P ? buf0 : buf1;
+      const bool has_next = t + 1 < ks.t1;
+      int e_q_next = 0;
+      float st = 0.f;
+      if (has_next) {
+        st = load_stats(t + 1);
+        stage(nxt, t + 1);
+        e_q_next = qexp[t + 1];
       }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-        dp_acc = mfma32(lds_row_frag(cur.dO, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
-      }
-      float dsv[16];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
-          if (KMASK && !ks.key_live) pe = 0.f;
-          dsv[4 * m + e] = pe * dp_acc[4 * m + e];
+      const float g = ldexpf(p.scale_log2, e_q + e_k);
+      bf16x8 dsf[4];
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
+        f32x16 s_acc = f32x16{}, dp_acc;
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(cur.ndelta + qb * 32 + 8 * m + 4 * half);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) dp_acc[4 * m + e] = nd[e];
         }
+  #pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
+          dp_acc = mfma32(lds_row_frag(cur.dO, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
+        }
+        float dsv[16];
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
+            if (KMASK && !ks.key_live) pe = 0.f;
+            dsv[4 * m + e] = pe * dp_acc[4 * m + e];
+          }
+        }
+        dsf[2 * qb] = pack_acc8(dsv);
+        dsf[2 * qb + 1] = pack_acc8(dsv + 8);
       }
-      dsf[2 * qb] = pack_acc8(dsv);
-      dsf[2 * qb + 1] = pack_acc8(dsv + 8);
+  #pragma unroll
+      for (int d = 0; d < 4; ++d) {
+  #pragma unroll
+        for (int qg = 0; qg < 4; ++qg) dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
+      }
+      if (has_next) {
+        wait_vmem();
+        store_stats(nxt, st);
+      }
+      __syncthreads();
+      e_q = e_q_next;
+    };
+    int t = ks.t0;
+    for (; t + 1 < ks.t1; t += 2) {
+      iteration(std::integral_constant<int, 0>{}, t);
+      iteration(std::integral_constant<int, 1>{}, t + 1);
     }
+    if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
+  }
+
+  if (ks.key_ok && p.q_split > 1) {
+    // fp32 partial (unscaled, unrotated) over this split's query tiles
+    float* row = p.part + ((((int64_t)ks.split * p.B + ks.b) * p.H + ks.h) * p.Lk + ks.j) * HD;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int qg = 0; qg < 4; ++qg) dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<f32x4*>(row + d * 32 + 8 * jq + 4 * half) =
+            f32x4{dk_acc[d][4 * jq], dk_acc[d][4 * jq + 1], dk_acc[d][4 * jq + 2], dk_acc[d][4 * jq + 3]};
     }
-    if (has_next) {
-      wait_vmem();
-      store_stats(nxt, st);
-    }
-    __syncthreads();
-    e_q = e_q_next;
-  };
-  int t = 0;
-  for (; t + 1 < ks.nt; t += 2) {
-    iteration(std::integral_constant<int, 0>{}, t);
-    iteration(std::integral_constant<int, 1>{}, t + 1);
-  }
-  if (t < ks.nt) iteration(std::integral_constant<int, 0>{}, t);
-
-  if (ks.key_ok) {
+  } else if (ks.key_ok) {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr) pos = token_pos(p.rope, ks.j);
     uint16_t* dkrow = p.dk + ((int64_t)ks.b * p.Lk * p.H + ks.h) * HD + (int64_t)ks.j * p.H * HD;
@@ -426,6 +460,34 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
         store_grad4(dkrow, p.rope, pos, d * 32 + 8 * jq + 4 * half, dk_acc[d][4 * jq] * p.scale,
                     dk_acc[d][4 * jq + 1] * p.scale, dk_acc[d][4 * jq + 2] * p.scale, dk_acc[d][4 * jq + 3] * p.scale);
     }
+  }
+}
+
+// Sum of the q_split partial dK~ and dV of every key (fixed order: deterministic),
+// then dk = R(p_j)^T scale dK~ and dv, in bf16.  One thread per 4 elements.
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p) {
+  const int64_t n4 = (int64_t)p.B * p.H * p.Lk * (HD / 4);
+  const int64_t part = (int64_t)p.q_split * p.B * p.H * p.Lk * HD;
+  const int64_t stride_s = (int64_t)p.B * p.H * p.Lk * HD;
+  RopeDev none = p.rope;
+  none.table = nullptr;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const int d0 = 4 * (int)(i % (HD / 4));
+    const int64_t r = i / (HD / 4);   // ((b * H) + h) * Lk + j
+    const int j = (int)(r % p.Lk);
+    const int64_t bh = r / p.Lk;
+    const int h = (int)(bh % p.H);
+    const int b = (int)(bh / p.H);
+    f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.q_split; ++s) {
+      sk += *reinterpret_cast<const f32x4*>(p.part + s * stride_s + r * HD + d0);
+      sv += *reinterpret_cast<const f32x4*>(p.part + part + s * stride_s + r * HD + d0);
+    }
+    TokenPos pos{0, 0, 0};
+    if (p.rope.table != nullptr) pos = token_pos(p.rope, j);
+    const int64_t off = (((int64_t)b * p.Lk + j) * p.H + h) * HD;
+    store_grad4(p.dk + off, p.rope, pos, d0, sk[0] * p.scale, sk[1] * p.scale, sk[2] * p.scale, sk[3] * p.scale);
+    store_grad4(p.dv + off, none, pos, d0, sv[0], sv[1], sv[2], sv[3]);
   }
 }
 
@@ -583,21 +645,27 @@ bool tiles_addressable(int L) {
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
   if (!tiles_addressable(p.Lq) || !tiles_addressable(p.Lk)) return hipErrorInvalidValue;
+  if (p.q_split < 1 || (p.q_split > 1 && p.part == nullptr)) return hipErrorInvalidValue;
   BwdParams q = p;
   q.n_tiles = (p.Lk + 32 * DV_WAVES - 1) / (32 * DV_WAVES);
-  int64_t total = (int64_t)q.n_tiles * p.H * p.B;
+  int64_t total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   if (p.k_lens != nullptr)
     hipLaunchKernelGGL(bwd_dv_kernel<true>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
   else
     hipLaunchKernelGGL(bwd_dv_kernel<false>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
   q.n_tiles = (p.Lk + 32 * DK_WAVES - 1) / (32 * DK_WAVES);
-  total = (int64_t)q.n_tiles * p.H * p.B;
+  total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   if (p.k_lens != nullptr)
     hipLaunchKernelGGL(bwd_dk_kernel<true>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);
   else
     hipLaunchKernelGGL(bwd_dk_kernel<false>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);
+  if (p.q_split > 1) {
+    const int64_t n4 = (int64_t)p.B * p.H * p.Lk * (HD / 4);
+    const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 65536);
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3(blocks), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ struct BwdParams {
   int B, Lq, Lk, H;         // q-side tensors [B, Lq, H, 128], k-side [B, Lk, H, 128]
   float scale;
   float scale_log2;
+  int q_split;              // dK/dV: query range split over this many workgroups per key block (>= 1)
+  float* part;              // q_split > 1: fp32 partial dK~ then dV, [q_split][B][H][Lk][128] each
   int n_tiles;              // set by the launchers
 };
 

@@ -1,4 +1,5 @@
 // Host-side argument checks of the wanattn C interface (see validate.h).
+#include <algorithm>
 #include "validate.h"
 
 #include <math.h>
@@ -74,6 +75,15 @@ Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D) {
   return w;
 }
 
+int bwd_q_split(int B, int Lq, int Lk, int H) {
+  const int64_t key_blocks = ((int64_t)Lk + 255) / 256 * H * B;   // dK workgroups without a split
+  if (key_blocks <= 0 || key_blocks >= 256) return 1;
+  const int64_t nt = ((int64_t)Lq + 63) / 64;
+  int64_t s = (512 + key_blocks - 1) / key_blocks;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, nt / 8));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 32));
+}
+
 BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
   BwdWsLayout w{};
   if (check_dims(B, Lq, H, D) != WANATTN_OK || check_dims(B, Lk, H, D) != WANATTN_OK) return w;
@@ -97,7 +107,14 @@ BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
   w.qexp = at;
   at = align256(at + qtiles * 4);
   w.kexp = at;
-  w.total = at + ktiles * 4;
+  at += ktiles * 4;
+  w.q_split = bwd_q_split(B, Lq, Lk, H);
+  w.part = 0;
+  if (w.q_split > 1) {
+    w.part = align256(at);
+    at = w.part + 2 * (size_t)w.q_split * B * H * Lk * (size_t)D * 4;
+  }
+  w.total = at;
   return w;
 }
 

@@ -36,13 +36,20 @@ struct Fp8WsLayout {
 };
 Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D);
 // Backward workspace: Delta (fp32 [B, H, L]), then the prep passes' tiles
-// (each [B, H, ceil(L/64)] x 16 KB) and the two exponent arrays (int32 per
-// tile); each part starts on a 256-byte boundary.
+// (each [B, H, ceil(L/64)] x 16 KB), the two exponent arrays (int32 per
+// tile) and, when the dK/dV passes split the query range (q_split > 1), their
+// fp32 partials (2 x q_split x [B, H, Lk, D]); each part starts on a 256-byte
+// boundary.
 struct BwdWsLayout {
-  size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, total;
+  size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, part, total;
+  int q_split;
 };
 // Query-side parts (Delta, qf, qt, dor, dot, qexp) over Lq tokens, key-side
 // parts (kf, kt, vr, kexp) over Lk.
+// Query-range split of the dK/dV passes: 1 while the key blocks alone give at
+// least 256 workgroups, else enough splits for ~512 (each >= 8 query tiles, at
+// most 32); their fp32 partials live in the backward workspace.
+int bwd_q_split(int B, int Lq, int Lk, int H);
 BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D);
 size_t self_bwd_ws_bytes(int B, int L, int H, int D, int with_rope);
 size_t cross_bwd_ws_bytes(int B, int Lq, int Lk, int H, int D);

@@ -76,6 +76,30 @@ def test_workspace_sizes(lib):
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, 64, 1) == 0
 
 
+def _q_split(B, Lq, Lk, H):
+    """Query-range split of the dK/dV passes: none while the key blocks of 256 give >= 256 workgroups."""
+    blocks = (Lk + 255) // 256 * H * B
+    if blocks >= 256:
+        return 1
+    s = -(-512 // blocks)
+    s = min(s, max(1, ((Lq + 63) // 64) // 8))
+    return max(1, min(s, 32))
+
+
+def test_cross_bwd_workspace_with_query_split(lib):
+    B, Lq, Lk, H, D = 1, 75600, 512, 40, 128          # 720p video tokens over 512 text tokens
+    assert _q_split(B, Lq, Lk, H) == 7
+    assert _q_split(1, 75600, 75600, 40) == 1          # the self-attention backward is not split
+    a256 = lambda x: (x + 255) // 256 * 256
+    qt, kt = B * H * ((Lq + 63) // 64), B * H * ((Lk + 63) // 64)
+    base = a256(B * H * Lq * 4) + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt
+    assert lib.wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D) == a256(base) + 2 * 7 * B * H * Lk * D * 4
+    # no split: the layout ends with the key tile exponents
+    qt, kt = 2 * 2 * 2, 2 * 2 * 8                      # 64-token tiles over B x H
+    assert lib.wanattn_cross_bwd_workspace_bytes(2, 100, 512, 2, D) == (
+        a256(2 * 2 * 100 * 4) + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt)
+
+
 def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P, scale=0.088,
          ws=P, ws_bytes=1 << 30):
     return lib.wanattn_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes, None)

@@ -272,6 +272,7 @@ def test_self_bwd_tiny_workload():
     (1, (3, 5, 7), 1, False, 1.0),
     (1, (4, 8, 8), 2, False, 4.0),      # peaked (exact operands, see the forward cases)
     (2, (3, 7, 9), 1, True, 1.0),
+    (1, (2, 32, 32), 1, True, 1.0),     # L = 2048, one key block: the dK/dV passes split the query range 4 ways
 ])
 def test_self_bwd_small(B, grid, H, rope_on, qmul):
     L = int(np.prod(grid))
