@@ -18,7 +18,7 @@
 // matching the accumulator registers), so no LDS transpose read is needed.
 // The inverse rotation is fused into the dQ and dK stores.
 //
-//  * bwd_dv:   workgroup = 128 keys (4 waves x 32, two workgroups per CU),
+//  * bwd_dv:   workgroup = 256 keys (8 waves x 32, one workgroup per CU),
 //    loop over 64-query tiles staged as Q fp16 rows and dO^T.  S = Q K^T
 //    (lane owns key j), dV^T += dO^T P with P from the accumulators.
 //  * bwd_dk:   workgroup = 256 keys (8 waves x 32, one workgroup per CU),
@@ -39,7 +39,7 @@ namespace wanattn {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int DV_WAVES = 4;
+constexpr int DV_WAVES = 8;
 constexpr int DK_WAVES = 8;
 constexpr int DQ_WAVES = 8;
 
@@ -113,11 +113,12 @@ __device__ __forceinline__ KeySide key_side(const BwdParams& p, int wave, int co
   return k;
 }
 
-// dV_j = sum_i P_ij dO_i.  Workgroup = 128 keys (4 waves, two workgroups per
-// CU); query tiles staged as Q fp16 rows and dO^T.  S = Q K^T from the
+// dV_j = sum_i P_ij dO_i.  Workgroup = 256 keys (8 waves, one workgroup per
+// CU: each query tile crosses from L2 once per CU, not once per 128 keys);
+// query tiles staged as Q fp16 rows and dO^T.  S = Q K^T from the
 // wave's K rows in registers, dV^T += dO^T P with P from the accumulators.
 template <bool KMASK>
-__global__ __launch_bounds__(64 * DV_WAVES, 2) void bwd_dv_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
   // Double-buffered tiles as separate objects, named statically in the
   // two-way unrolled loop (LDS reads do not wait for copies in flight).
   __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
@@ -145,9 +146,10 @@ __global__ __launch_bounds__(64 * DV_WAVES, 2) void bwd_dv_kernel(BwdParams p) {
   for (int d = 0; d < 4; ++d) dv_acc[d] = f32x16{};
   const float* lse_row = p.lse + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
 
-  uint32_t roff[4], toff[4];
+  constexpr int NCP = 16 / DV_WAVES;   // 1 KB copies per wave and tile
+  uint32_t roff[NCP], toff[NCP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NCP; ++i) {
     roff[i] = rowtile_lane_off<DV_WAVES>(wv, i, lane);
     toff[i] = ttile_lane_off<DV_WAVES>(wv, i, lane);
   }
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(64 * DV_WAVES, 2) void bwd_dv_kernel(BwdParams p) {
   auto stage = [&](const Buf& dst, int t) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NCP; ++i) {
       buf_dma16(qfr, roff[i], soff, tile_lds_block<DV_WAVES>(dst.q, wv, i));
       buf_dma16(dotr, toff[i], soff, tile_lds_block<DV_WAVES>(dst.dOt, wv, i));
     }
