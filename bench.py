@@ -177,8 +177,8 @@ def bench_next_rows(wa, torch, synth, dev, rope):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the heads or key blocks would shard across GPUs; see the design notes)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(heads would split across GPUs by an all-to-all, key blocks by ring passes)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
