@@ -36,27 +36,41 @@ struct TileFrag {
 __device__ __forceinline__ int frag_token(int tid, int it) { return (tid >> 4) + 16 * it; }
 __device__ __forceinline__ int frag_chunk(int tid) { return tid & 15; }
 
-// Load tokens [64*tile, +64) of head (b, h) of a [B, L, H, 128] bf16 tensor,
-// optionally rotated (fp32), and return this thread's max |x|.
-// Tokens at or past `valid` (<= L) are zero; `pos0` is the RoPE token index of row 0.
-__device__ __forceinline__ float load_tile(TileFrag& f, const uint16_t* __restrict__ x, int b, int h, int tile, int L,
-                                           int H, const RopeDev* rope, int tid, int valid, int pos0) {
+// Tokens [64*tile, +64) of head (b, h) of a [B, L, H, 128] bf16 tensor as raw
+// bf16 pairs (16 bytes per thread and row).  Tokens at or past `valid` (<= L)
+// are zero.  The loads are only issued here: a kernel issues all of its loads
+// before it uses any of them, so their latencies overlap.
+struct TileRaw {
+  u32x4 v[4];
+};
+__device__ __forceinline__ void load_raw(TileRaw& r, const uint16_t* __restrict__ x, int b, int h, int tile, int L,
+                                         int H, int tid, int valid) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int n = tile * TILE_ROWS + frag_token(tid, it);
+    r.v[it] = u32x4{0u, 0u, 0u, 0u};
+    if (n < valid) r.v[it] = *reinterpret_cast<const u32x4*>(x + (((int64_t)b * L + n) * H + h) * HD + frag_chunk(tid) * 8);
+  }
+}
+
+// The raw tile in fp32, optionally rotated; returns this thread's max |x|.
+// `pos0` is the RoPE token index of row 0.
+__device__ __forceinline__ float convert_tile(TileFrag& f, const TileRaw& r, int tile, const RopeDev& rope, bool rotate,
+                                              int tid, int valid, int pos0) {
   float m = 0.f;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int n = tile * TILE_ROWS + frag_token(tid, it);
     const int ch = frag_chunk(tid);
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (n < valid) v = *reinterpret_cast<const u32x4*>(x + (((int64_t)b * L + n) * H + h) * HD + ch * 8);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      f.x[it][2 * t] = bf16_lo(v[t]);
-      f.x[it][2 * t + 1] = bf16_hi(v[t]);
+      f.x[it][2 * t] = bf16_lo(r.v[it][t]);
+      f.x[it][2 * t + 1] = bf16_hi(r.v[it][t]);
     }
-    if (rope != nullptr && n < valid) {
-      const TokenPos pos = token_pos(*rope, pos0 + n);
+    if (rotate && n < valid) {
+      const TokenPos pos = token_pos(rope, pos0 + n);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rope_rotate(f.x[it][2 * t], f.x[it][2 * t + 1], rope_cs(*rope, pos, 4 * ch + t), false);
+      for (int t = 0; t < 4; ++t) rope_rotate(f.x[it][2 * t], f.x[it][2 * t + 1], rope_cs(rope, pos, 4 * ch + t), false);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(f.x[it][e]));
@@ -64,12 +78,13 @@ __device__ __forceinline__ float load_tile(TileFrag& f, const uint16_t* __restri
   return m;
 }
 
-// Max over the 256 threads (every thread gets it).  Ends with a barrier.
+// Max over the 256 threads (every thread gets it).  Ends with a barrier that
+// orders LDS only: the global stores already issued stay in flight.
 __device__ __forceinline__ float block_max(float m, float* wmax, int tid) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
+  lds_barrier();
   return fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
@@ -139,8 +154,11 @@ __global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restric
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
   const int valid = lens != nullptr ? min(max(lens[b], 0), L) : L;
+  TileRaw rk, rv;
+  load_raw(rk, k, b, h, tile, L, H, tid, valid);
+  load_raw(rv, v, b, h, tile, L, H, tid, valid);
   TileFrag f;
-  const float mk = load_tile(f, k, b, h, tile, L, H, F16 ? &rope : nullptr, tid, valid, pos0);
+  const float mk = convert_tile(f, rk, tile, rope, F16, tid, valid, pos0);
   if (F16) {
     const int e = pow2_exponent_15(block_max(mk, wmax, tid));
     if (tid == 0) kexp[blockIdx.x] = e;
@@ -148,9 +166,9 @@ __global__ __launch_bounds__(256) void kv_tiles_kernel(const uint16_t* __restric
   } else {
     store_row_tile_bf16(kt + off, f, tid);
   }
-  load_tile(f, v, b, h, tile, L, H, nullptr, tid, valid, 0);
+  convert_tile(f, rv, tile, rope, false, tid, valid, 0);
   stage_bf16(s, f, tid);
-  __syncthreads();
+  lds_barrier();
   store_t_tile(vt + off, s, tid);
 }
 
@@ -169,15 +187,18 @@ __global__ __launch_bounds__(256) void bwd_k_tiles_kernel(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
   const int valid = lens != nullptr ? min(max(lens[b], 0), L) : L;
+  TileRaw rk, rv;
+  load_raw(rk, k, b, h, tile, L, H, tid, valid);
+  load_raw(rv, v, b, h, tile, L, H, tid, valid);
   TileFrag f;
-  const float mk = load_tile(f, k, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid, valid, 0);
+  const float mk = convert_tile(f, rk, tile, rope, rope.table != nullptr, tid, valid, 0);
   const int e = pow2_exponent_15(block_max(mk, wmax, tid));
   if (tid == 0) kexp[blockIdx.x] = e;
   store_row_tile_f16(kf + off, f, e, tid);
   stage_bf16(s, f, tid);
-  __syncthreads();
+  lds_barrier();
   store_t_tile(kt + off, s, tid);
-  load_tile(f, v, b, h, tile, L, H, nullptr, tid, valid, 0);
+  convert_tile(f, rv, tile, rope, false, tid, valid, 0);
   store_row_tile_bf16(vr + off, f, tid);
 }
 
@@ -197,22 +218,26 @@ __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __rest
   const int b = bh / H;
   const int tid = threadIdx.x;
   const int64_t off = (int64_t)blockIdx.x * TILE_ELEMS;
+  TileRaw rq, rd, ro;
+  load_raw(rq, q, b, h, tile, L, H, tid, L);
+  load_raw(rd, dout, b, h, tile, L, H, tid, L);
+  load_raw(ro, o, b, h, tile, L, H, tid, L);
   TileFrag f;
-  const float mq = load_tile(f, q, b, h, tile, L, H, rope.table != nullptr ? &rope : nullptr, tid, L, 0);
+  const float mq = convert_tile(f, rq, tile, rope, rope.table != nullptr, tid, L, 0);
   const int e = pow2_exponent_15(block_max(mq, wmax, tid));
   if (tid == 0) qexp[blockIdx.x] = e;
   store_row_tile_f16(qf + off, f, e, tid);
   stage_bf16(s, f, tid);
-  __syncthreads();
+  lds_barrier();
   store_t_tile(qt + off, s, tid);
-  __syncthreads();   // the staging rows are reused below
+  lds_barrier();   // the staging rows are reused below
 
   // dO: row tile, T tile, and Delta = <dO, O> per token (16 lanes per row).
-  load_tile(f, dout, b, h, tile, L, H, nullptr, tid, L, 0);
+  convert_tile(f, rd, tile, rope, false, tid, L, 0);
   store_row_tile_bf16(dor + off, f, tid);
   stage_bf16(s, f, tid);
   TileFrag g;
-  load_tile(g, o, b, h, tile, L, H, nullptr, tid, L, 0);
+  convert_tile(g, ro, tile, rope, false, tid, L, 0);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     float d = 0.f;
@@ -225,7 +250,7 @@ __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __rest
     const int n = tile * TILE_ROWS + frag_token(tid, it);
     if (frag_chunk(tid) == 0 && n < L) delta[((int64_t)b * H + h) * L + n] = d;
   }
-  __syncthreads();
+  lds_barrier();
   store_t_tile(dot + off, s, tid);
 }
 
