@@ -87,12 +87,13 @@ namespace {
 // index of the first query / key row.
 int run_self_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Lq, int Lk, int H,
                  int D, wanattn_grid g, wanattn_rope r, const float* table, float scale, void* ws,
-                 const int32_t* lens, int q_pos0, int k_pos0, hipStream_t s) {
+                 const int32_t* lens, int q_pos0, int k_pos0, bool tail_split, hipStream_t s) {
   const RopeDev rope = make_rope(g, r, table);
   // K (with RoPE rotated once, instead of on every query tile's visit, and
   // stored in fp16 with a power-of-two exponent per tile) and V are rewritten
   // in the forward's 64-key tile layout in one pass; queries are rotated on
   // load.
+  // The tail split (self-attention, Lq == Lk) keeps its partials after the tiles.
   const FwdWsLayout wl = self_fwd_ws_layout(B, Lk, H, D, table != nullptr);
   uint16_t* kt = (uint16_t*)((uint8_t*)ws + wl.kt);
   uint16_t* vt = (uint16_t*)((uint8_t*)ws + wl.vt);
@@ -119,6 +120,7 @@ int run_self_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.Lk = Lk;
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
+  p.part = (tail_split && wl.part != 0) ? (float*)((uint8_t*)ws + wl.part) : nullptr;
   return hip_status(launch_attn_fwd(p, s));
 }
 
@@ -130,7 +132,7 @@ WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, vo
                                  void* ws, size_t ws_bytes, void* stream) {
   const int rc = validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes);
   if (rc != WANATTN_OK) return rc;
-  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, nullptr, 0, 0, (hipStream_t)stream);
+  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, nullptr, 0, 0, true, (hipStream_t)stream);
 }
 
 WANATTN_API size_t wanattn_self_fwd_fp8_workspace_bytes(int B, int L, int H, int D) {
@@ -172,11 +174,11 @@ WANATTN_API int wanattn_self_fwd_varlen(const void* q, const void* k, const void
                                         void* stream) {
   const int rc = validate_self_fwd_varlen(q, k, v, o, lse, seq_lens, B, L, H, D, g, r, table, scale, ws, ws_bytes);
   if (rc != WANATTN_OK) return rc;
-  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, seq_lens, 0, 0, (hipStream_t)stream);
+  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, seq_lens, 0, 0, true, (hipStream_t)stream);
 }
 
 WANATTN_API size_t wanattn_partial_fwd_workspace_bytes(int B, int Lk, int H, int D, int with_rope) {
-  return self_fwd_ws_bytes(B, Lk, H, D, with_rope);
+  return fwd_tiles_ws_bytes(B, Lk, H, D, with_rope);
 }
 
 WANATTN_API int wanattn_partial_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Lq,
@@ -186,7 +188,7 @@ WANATTN_API int wanattn_partial_fwd(const void* q, const void* k, const void* v,
   const int rc =
       validate_partial_fwd(q, k, v, o, lse, B, Lq, Lk, H, D, g, r, table, q_offset, k_offset, scale, ws, ws_bytes);
   if (rc != WANATTN_OK) return rc;
-  return run_self_fwd(q, k, v, o, lse, B, Lq, Lk, H, D, g, r, table, scale, ws, nullptr, q_offset, k_offset,
+  return run_self_fwd(q, k, v, o, lse, B, Lq, Lk, H, D, g, r, table, scale, ws, nullptr, q_offset, k_offset, false,
                       (hipStream_t)stream);
 }
 

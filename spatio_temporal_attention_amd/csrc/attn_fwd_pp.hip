@@ -45,6 +45,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "validate.h"
 
 namespace wanattn {
 
@@ -67,8 +68,10 @@ constexpr float PSUM_LIMIT = 65536.0f;    // largest partial row sum of P kept w
 // the early ones one after their last.
 constexpr int PP_WAVES = 8;
 constexpr int PP_BR = 32 * PP_WAVES;   // query rows per workgroup
+static_assert(PP_BR == FWD_ROWS, "the tail split and its workspace assume 256-row workgroups");
 
-template <bool POS_SCALE, bool F16>
+// SPLIT: the tail launch (one key range of a query tile, fp32 partial out).
+template <bool POS_SCALE, bool F16, bool SPLIT>
 // Two waves per SIMD by design (one workgroup per CU); without the explicit
 // target the compiler aims for four (the LDS would allow two workgroups) and
 // schedules for register pressure instead of latency.
@@ -88,7 +91,13 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const bool late = wv >= PP_WAVES / 2;   // waves 4..7: one phase behind
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  int logical, split = 0;
+  if (SPLIT) {
+    logical = p.qt_base + (int)blockIdx.x / p.n_split;
+    split = (int)blockIdx.x % p.n_split;
+  } else {
+    logical = xcd_remap(blockIdx.x, gridDim.x);
+  }
   const int qt = logical % p.n_qtiles;
   const int bh = logical / p.n_qtiles;
   const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
@@ -163,8 +172,15 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   float l_run = 0.f;
   const_i32* kexp = F16 ? const_ptr(p.kexp + tile0) : nullptr;   // scalar loads
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
+  // Key tiles [t_begin, t_end): all of them, or one of p.n_split ranges.
+  int t_begin = 0, t_end = n_tiles;
+  if (SPLIT) {
+    const int chunk = (n_tiles + p.n_split - 1) / p.n_split;
+    t_begin = min(n_tiles, split * chunk);
+    t_end = min(n_tiles, t_begin + chunk);
+  }
 
-  if (n_tiles > 0) {
+  if (t_end > t_begin) {
     // Each wave copies 1/8 of every K and V tile (2 x 1 KB each).
     uint32_t koff[2], voff[2];
 #pragma unroll
@@ -278,15 +294,15 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
     };
 
     // Prologue: K(0), V(0), K(1) staged; S(0) by every wave.
-    stage_k(k_lds0, 0);
-    stage_v(v_lds0, 0);
-    if (n_tiles > 1) stage_k(k_lds1, 1);
-    int e_nxt = F16 ? kexp[0] : 0;   // exponent of the next tile to take its softmax
+    stage_k(k_lds0, t_begin);
+    stage_v(v_lds0, t_begin);
+    if (t_begin + 1 < t_end) stage_k(k_lds1, t_begin + 1);
+    int e_nxt = F16 ? kexp[t_begin] : 0;   // exponent of the next tile to take its softmax
     wait_vmem();
     __syncthreads();
     scores(k_lds0);
-    const int last = n_tiles - 1;
-    const bool partial = n_keys % FWD_BC != 0;
+    const int last = t_end - 1;
+    const bool partial = n_keys % FWD_BC != 0 && t_end == n_tiles;   // only the last key tile is partial
     if (late) __syncthreads();   // the early waves run softmax(0) meanwhile
 
     // Tile t with parity P = t & 1: K(t+1) in K buffer 1-P, V(t) in V buffer
@@ -301,13 +317,13 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
       // barrier 2t), the early ones in their products phase; each waits for
       // its own before the barrier that ends its products phase.
       if (late) {
-        if (t + 2 < n_tiles) stage_k(k_fill, t + 2);
-        if (t + 1 < n_tiles) stage_v(v_fill, t + 1);
+        if (t + 2 < t_end) stage_k(k_fill, t + 2);
+        if (t + 1 < t_end) stage_v(v_fill, t + 1);
       }
       // Tile t's exponent was loaded one tile earlier; load tile t+1's now
       // (scalar load, needed after two barriers).
       const int e_t = e_nxt;
-      if (F16 && t + 1 < n_tiles) e_nxt = kexp[t + 1];
+      if (F16 && t + 1 < t_end) e_nxt = kexp[t + 1];
       if constexpr (POS_SCALE) {
         // The partial last tile: keys past n_keys get a score of -inf in
         // place (exact under the positive factor), so one softmax serves
@@ -328,8 +344,8 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
       }
       __syncthreads();   // barrier 2t (early waves), 2t+1 (late waves)
       if (!late) {
-        if (t + 2 < n_tiles) stage_k(k_fill, t + 2);
-        if (t + 1 < n_tiles) stage_v(v_fill, t + 1);
+        if (t + 2 < t_end) stage_k(k_fill, t + 2);
+        if (t + 1 < t_end) stage_v(v_fill, t + 1);
       }
       pv_product(v_cur);
       if (t < last) {
@@ -346,16 +362,32 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
         __syncthreads();   // barrier 2t+1 (early), 2t+2 (late)
       }
     };
-    int t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
       tile(std::integral_constant<int, 0>{}, t);
       tile(std::integral_constant<int, 1>{}, t + 1);
     }
-    if (t < n_tiles) tile(std::integral_constant<int, 0>{}, t);
+    if (t < t_end) tile(std::integral_constant<int, 0>{}, t);
     if (!late) __syncthreads();   // matches the late waves' barrier before their last products phase
   }
 
   const float l_tot = xor32_sum(l_run);
+  if (SPLIT) {
+    // Partial of this key range: O unnormalized, the running max m (log2
+    // units; -inf for an empty range) and l = sum of P against it.
+    float* dst = p.part + ((int64_t)blockIdx.x * PP_BR + wave * 32 + col) * FWD_PART_FLOATS;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<f32x4*>(dst + d * 32 + 8 * jq + 4 * half) =
+            f32x4{o_acc[d][4 * jq], o_acc[d][4 * jq + 1], o_acc[d][4 * jq + 2], o_acc[d][4 * jq + 3]};
+    if (half == 0) {
+      dst[128] = m_run;
+      dst[129] = l_tot;
+    }
+    return;
+  }
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (row_ok) {
     uint16_t* orow = p.o + ((int64_t)b * p.Lq * p.H + h) * HD + (int64_t)i * q_row_stride;
@@ -376,6 +408,49 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   }
 }
 
+// Merge of the tail split's partials: per query row, m = max over the key
+// ranges of m_s, l = sum_s l_s 2^(m_s - m), O = sum_s O_s 2^(m_s - m) / l and
+// LSE = ln 2 (m + log2 l) (fixed order over s).  One thread per row and four
+// head-dim columns.
+__global__ __launch_bounds__(256) void fwd_split_merge_kernel(FwdParams p, int tail) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c4 = (int)(idx & 31);
+  const int64_t rr = idx >> 5;
+  const int rl = (int)(rr % PP_BR);
+  const int ti = (int)(rr / PP_BR);
+  if (ti >= tail) return;
+  const int logical = p.qt_base + ti;
+  const int qt = logical % p.n_qtiles;
+  const int bh = logical / p.n_qtiles;
+  const int b = bh % p.B;
+  const int h = bh / p.B;
+  int n_q = p.Lq;
+  if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
+  const int i = qt * PP_BR + rl;
+  if (i >= n_q) return;
+  const int64_t stride = (int64_t)PP_BR * FWD_PART_FLOATS;
+  const float* base = p.part + ((int64_t)ti * p.n_split * PP_BR + rl) * FWD_PART_FLOATS;
+  float m = -INFINITY;
+  for (int s = 0; s < p.n_split; ++s) m = fmaxf(m, base[s * stride + 128]);
+  float l = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (m > -INFINITY) {
+    for (int s = 0; s < p.n_split; ++s) {
+      const float w = __builtin_amdgcn_exp2f(base[s * stride + 128] - m);   // 0 for an empty range
+      l += base[s * stride + 129] * w;
+      const f32x4 o4 = *reinterpret_cast<const f32x4*>(base + s * stride + 4 * c4);
+      acc += o4 * w;
+    }
+  }
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  u32x2 w2;
+  w2[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+  w2[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(p.o + (((int64_t)b * p.Lq + i) * p.H + h) * HD + 4 * c4) = w2;
+  if (c4 == 0 && p.lse != nullptr)
+    p.lse[((int64_t)b * p.H + h) * p.Lq + i] = (l > 0.f) ? (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
@@ -388,13 +463,35 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
   r.n_qtiles = (p.Lq + PP_BR - 1) / PP_BR;
   const int64_t n = (int64_t)r.n_qtiles * p.H * p.B;
   if (n <= 0 || n > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)n), block(64 * PP_WAVES);
-  if (p.scale_log2 > 0.f) {
-    if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true>), grid, block, 0, stream, r);
-    else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false>), grid, block, 0, stream, r);
-  } else {
-    if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true>), grid, block, 0, stream, r);
-    else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false>), grid, block, 0, stream, r);
+  // The tail split follows the rule the workspace was sized by.
+  FwdSplit sp{(int)n, (int)n, 0, 1};
+  if (p.part != nullptr) sp = fwd_tail_split(p.B, p.Lq, p.H);
+  if (sp.n != n) return hipErrorInvalidValue;
+  const bool pos = p.scale_log2 > 0.f;
+  const dim3 block(64 * PP_WAVES);
+  if (sp.n_main > 0) {
+    const dim3 grid((unsigned)sp.n_main);
+    if (pos) {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false>), grid, block, 0, stream, r);
+    } else {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false>), grid, block, 0, stream, r);
+    }
+  }
+  if (sp.tail > 0) {
+    r.qt_base = sp.n_main;
+    r.n_split = sp.S;
+    const dim3 grid((unsigned)(sp.tail * sp.S));
+    if (pos) {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, true>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, true>), grid, block, 0, stream, r);
+    } else {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, true>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, true>), grid, block, 0, stream, r);
+    }
+    hipLaunchKernelGGL(fwd_split_merge_kernel, dim3((unsigned)(sp.tail * (PP_BR * 32 / 256))), dim3(256), 0, stream,
+                       r, sp.tail);
   }
   return hipGetLastError();
 }

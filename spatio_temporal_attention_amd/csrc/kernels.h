@@ -27,6 +27,10 @@ struct FwdParams {
   int B, Lq, Lk, H;
   float scale_log2;         // softmax scale * log2(e)
   int n_qtiles;             // set by the launcher
+  // Tail split (self-attention only): fp32 partials of the last query tiles'
+  // key ranges (nullptr: no split); qt_base and n_split are set by the launcher.
+  float* part;
+  int qt_base, n_split;
 };
 
 // Self-attention backward over the prep passes' tiles: [B, H, ceil(L/64)]

@@ -44,8 +44,22 @@ int64_t rope_table_entries(wanattn_grid g, wanattn_rope r) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
-  FwdWsLayout w{0, 0, 0, 0};
+FwdSplit fwd_tail_split(int B, int Lq, int H) {
+  const int64_t n64 = (int64_t)B * H * (((int64_t)Lq + FWD_ROWS - 1) / FWD_ROWS);
+  const int n = (int)std::min<int64_t>(n64, 0x7fffffff);
+  FwdSplit sp{n, n, 0, 1};
+  if (n64 < 4 * FWD_ROUND || n % FWD_ROUND == 0) return sp;
+  const int tail = n % FWD_ROUND;
+  const int S = std::min(8, FWD_ROUND / tail);
+  if (S < 2) return sp;
+  sp.n_main = n - tail;
+  sp.tail = tail;
+  sp.S = S;
+  return sp;
+}
+
+static FwdWsLayout fwd_tiles_layout(int B, int L, int H, int D, int with_rope) {
+  FwdWsLayout w{0, 0, 0, 0, 0};
   if (check_dims(B, L, H, D) != WANATTN_OK) return w;
   const size_t tiles = (size_t)B * H * (((size_t)L + 63) / 64);
   const size_t tile_elems = tiles * 64 * (size_t)D;
@@ -59,8 +73,23 @@ FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
   return w;
 }
 
+FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
+  FwdWsLayout w = fwd_tiles_layout(B, L, H, D, with_rope);
+  if (w.total == 0) return w;
+  const FwdSplit sp = fwd_tail_split(B, L, H);
+  if (sp.tail > 0) {
+    w.part = align256(w.total);
+    w.total = w.part + (size_t)sp.tail * sp.S * FWD_ROWS * FWD_PART_FLOATS * 4;
+  }
+  return w;
+}
+
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope) {
   return self_fwd_ws_layout(B, L, H, D, with_rope).total;
+}
+
+size_t fwd_tiles_ws_bytes(int B, int L, int H, int D, int with_rope) {
+  return fwd_tiles_layout(B, L, H, D, with_rope).total;
 }
 
 Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D) {
@@ -188,7 +217,7 @@ int validate_partial_fwd(const void* q, const void* k, const void* v, const void
   const void* bufs[] = {q, k, v, o};
   for (const void* p : bufs) WANATTN_TRY(check_bf16(p));
   if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
-  if (ws == nullptr || ws_bytes < self_fwd_ws_bytes(B, Lk, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
+  if (ws == nullptr || ws_bytes < fwd_tiles_ws_bytes(B, Lk, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
   return WANATTN_OK;
 }

@@ -20,15 +20,35 @@ int check_scale(float scale);
 bool aligned(const void* p, size_t a);
 int64_t rope_table_entries(wanattn_grid g, wanattn_rope r);   // (cos, sin) pairs; -1 if invalid
 
+// Tail split of the self-attention forward.  Its workgroups take 256 query
+// rows each, FWD_ROUND of them run at once (one per CU of an MI355X); when
+// there are at least four rounds and the count n is not a multiple of the
+// round, the last tail = n % FWD_ROUND query tiles would run alone on a few
+// CUs.  They run instead as S = FWD_ROUND / tail (at most 8) key ranges each,
+// whose fp32 partials a merge pass combines exactly.  S < 2: no split.
+constexpr int FWD_ROUND = 256;
+constexpr int FWD_ROWS = 256;          // query rows per forward workgroup
+constexpr int FWD_PART_FLOATS = 132;   // per partial row: O (128, unnormalized), m (log2), l, 2 pad (16-byte rows)
+struct FwdSplit {
+  int n;        // workgroups of the whole forward
+  int n_main;   // workgroups of the main launch (the first n_main query tiles)
+  int tail;     // query tiles of the split launch (0: no split)
+  int S;        // key ranges per tail tile
+};
+FwdSplit fwd_tail_split(int B, int Lq, int H);
+
 // Forward workspace, in 64-key tiles of every (b, h): K (bf16, or with RoPE
 // the rotated keys in fp16 with a power-of-two exponent per tile), V^T
-// (bf16), then with RoPE the tile exponents (int32); each part starts on a
-// 256-byte boundary.
+// (bf16), then with RoPE the tile exponents (int32), then (self-attention
+// with a tail split only) the fp32 partials [tail * S][FWD_ROWS][132]; each
+// part starts on a 256-byte boundary.
 struct FwdWsLayout {
-  size_t kt, vt, kexp, total;   // byte offsets of the parts and the total size
+  size_t kt, vt, kexp, part, total;   // byte offsets of the parts and the total size (part: 0 if none)
 };
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope);
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);
+// The key/value tiles alone (the shard forward, whose query and key lengths differ, takes no split).
+size_t fwd_tiles_ws_bytes(int B, int L, int H, int D, int with_rope);
 // FP8 forward workspace: K and V^T e4m3 tiles ([B, H, ceil(L/64)] x 8 KB each), then
 // their int32 exponents; each part on a 256-byte boundary.
 struct Fp8WsLayout {

@@ -65,9 +65,21 @@ def test_workspace_sizes(lib):
     tiled = B * H * ((L + 63) // 64) * 64 * D           # elements of K or V in 64-key tiles, zero-padded
     assert tiled > n
     n_tiles = B * H * ((L + 63) // 64)
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == 2 * tiled * 2          # K and V^T tiles
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + 4 * n_tiles  # + tile exponents
+    # 11,840 query tiles of 256 rows = 46 rounds of 256 + 64: the last 64 run as 4 key ranges each, whose
+    # fp32 partials (rows of 132 floats) follow the tiles on a 256-byte boundary
+    part = 64 * 4 * 256 * 132 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == up(2 * tiled * 2) + part
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == up(2 * tiled * 2 + 4 * n_tiles) + part
+    assert lib.wanattn_partial_fwd_workspace_bytes(B, L, H, D, 0) == 2 * tiled * 2          # K and V^T tiles
+    assert lib.wanattn_partial_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + 4 * n_tiles  # + exponents
     assert lib.wanattn_self_fwd_workspace_bytes(1, 1, 1, D, 0) == 2 * 64 * D * 2
+    # no split below four rounds, or on a multiple of 256 tiles (32 heads: 9,472 = 37 x 256)
+    small = B * 32 * ((L + 63) // 64) * 64 * D
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, 32, D, 0) == 2 * small * 2
+    assert lib.wanattn_self_fwd_workspace_bytes(1, 2048, 127, D, 0) == 2 * 127 * 2048 * D * 2     # 1,016 tiles
+    # 1,040 tiles: the last 16 split 8 ways
+    assert lib.wanattn_self_fwd_workspace_bytes(1, 2048, 130, D, 0) == 2 * 130 * 2048 * D * 2 + 16 * 8 * 256 * 132 * 4
     delta = (B * H * L * 4 + 255) // 256 * 256
     exps = (4 * n_tiles + 255) // 256 * 256 + 4 * n_tiles
     # Delta, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents

@@ -1,0 +1,96 @@
+"""GPU parity of the self-attention forward's tail split against the fp64 oracle.
+
+The forward runs 256-row query tiles, 256 at a time; when a large problem's
+tile count n is not a multiple of 256, the last n % 256 tiles run as several
+key ranges each whose fp32 partials are merged exactly.  These shapes put the
+split on known heads (logical tile = (head * B + item) * tiles_per_head + qt,
+batch item innermost) and check those heads in full; same bar as the other
+parity tests (max-abs 2e-2, rel-L2 5e-3 on O; |LSE error| 1e-3)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bf16_to_f64, check_close, check_lse, f32_to_np, to_dev
+from oracle import RopeSpec
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import spatio_temporal_attention_amd as wa  # noqa: E402
+
+ROPE = RopeSpec()
+SCALE = 1.0 / math.sqrt(128)
+GRID = (2, 32, 32)        # L = 2048: 8 query tiles of 256 rows, 32 key tiles of 64 per head
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    wa.lib()
+
+
+def _split_rule(B, L, H):
+    """(main tiles, tail tiles, key ranges) of the documented split rule."""
+    n = B * H * ((L + 255) // 256)
+    if n < 1024 or n % 256 == 0:
+        return n, 0, 1
+    tail = n % 256
+    S = min(8, 256 // tail)
+    return (n, 0, 1) if S < 2 else (n - tail, tail, S)
+
+
+def test_tail_split_heads_match_oracle():
+    B, H = 1, 130
+    L = int(np.prod(GRID))
+    n_main, tail, S = _split_rule(B, L, H)
+    assert (n_main, tail, S) == (1024, 16, 8)     # heads 128 and 129 run split, 8 key ranges of 4 tiles
+    q, k, v = (synth.random_bf16(9100 + i, (B, L, H, 128)) for i in range(3))
+    o, lse = wa.self_fwd(to_dev(q), to_dev(k), to_dev(v), grid=GRID, table=wa.rope_table(GRID, ROPE), rope=ROPE,
+                         scale=SCALE)
+    torch.cuda.synchronize()
+    go, gl = bf16_to_f64(o), f32_to_np(lse)
+    heads = [128, 129, 0]                          # the two split heads, and one of the main launch
+    f = synth.bf16_bits_to_f64
+    ro, rl = oracle.self_fwd_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), SCALE, GRID, ROPE)
+    for j, h in enumerate(heads):
+        print(f"  head {h}:")
+        check_close("O", go[:, :, h], ro[:, :, j])
+        check_lse("LSE", gl[:, h], rl[:, j])
+
+
+def test_tail_split_varlen_masked_ranges_and_rows():
+    """Two items (lengths 2048 and 1500, so 32 and 24 key tiles, the last one partial) with 65 heads: the
+    tail is head 64 of both items, split 8 ways; rows past an item's length stay unwritten."""
+    B, H = 2, 65
+    L = int(np.prod(GRID))
+    n_main, tail, S = _split_rule(B, L, H)
+    assert (n_main, tail, S) == (1024, 16, 8)
+    lens = np.array([2048, 1500], dtype=np.int32)
+    q, k, v = (synth.random_bf16(9200 + i, (B, L, H, 128)) for i in range(3))
+    nan_bits = np.uint16(0x7FC0)
+    for b, n in enumerate(lens):                   # padding holds NaN: must never be read
+        q[b, n:] = nan_bits
+        k[b, n:] = nan_bits
+        v[b, n:] = nan_bits
+    o = torch.full((B, L, H, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, L), 5.0, dtype=torch.float32, device="cuda")
+    wa.self_fwd_varlen(to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(lens).cuda(), grid=GRID,
+                       table=wa.rope_table(GRID, ROPE), rope=ROPE, scale=SCALE, out=o, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = bf16_to_f64(o), f32_to_np(lse)
+    heads = [64, 3]                                # the split head, and one of the main launch
+    f = synth.bf16_bits_to_f64
+    ro, rl = oracle.self_fwd_varlen_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), lens, SCALE, GRID,
+                                        ROPE)
+    for j, h in enumerate(heads):
+        for b, n in enumerate(lens):
+            print(f"  head {h}, item {b} (len {n}):")
+            check_close("O", go[b, :n, h], ro[b, :n, j])
+            check_lse("LSE", gl[b, h, :n], rl[b, j, :n])
+            assert np.all(go[b, n:, h] == 7.0), "rows past the length were written"
+            assert np.all(gl[b, h, n:] == 5.0), "LSE past the length was written"
