@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_720p_hbm_traffic.json")
-FWD_SOURCES = ("attn_fwd_pp.hip", "common.h", "kernels.h")
+FWD_SOURCES = ("attn_fwd_pp.hip", "common.h", "kernels.h", "validate.h", "validate.cpp")
 
 
 def measured_traffic():
@@ -308,7 +308,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
-                     "kernel": "attn_fwd_pp_kernel (+ the K/V tile prep pass inside the same timed call)",
+                     "kernel": "attn_fwd_pp_kernel (+ the K/V tile prep pass, the tail-split launch and its merge, inside the same timed call)",
                      "flop_per_launch": fwd_flop},
     }
     result.update(extra)

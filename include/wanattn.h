@@ -128,8 +128,13 @@ int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D,
  * a table the rotated keys in fp16 with one power-of-two exponent per tile,
  * the exponents following as int32 [B, H, ceil(L/64)]) and V transposed as
  * [B, H, ceil(L/64), D, 64] bf16 (the PV product's operand layout); each
- * part starts on a 256-byte boundary.  Its contents on return are
- * unspecified.
+ * part starts on a 256-byte boundary.  Large problems add one more part: the
+ * kernel runs 256-row query tiles 256 at a time, and when their count
+ * n = B*H*ceil(L/256) is at least 1024 and not a multiple of 256, the last
+ * t = n % 256 tiles run as S = min(8, 256/t) key ranges each (no split if
+ * S < 2), whose fp32 partials ([t*S][256 rows][132 floats]) a merge pass
+ * combines exactly; the size function accounts for them.  Its contents on
+ * return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 
@@ -216,7 +221,8 @@ int wanattn_self_fwd_varlen(const void* q, const void* k, const void* v, void* o
  * ([B, H, Lq], may be NULL) are the attention of the shard's queries over the
  * shard's keys only; wanattn_lse_merge combines the shards exactly.  table ==
  * NULL: no rotation (g and the offsets only need to be >= 0).
- * Workspace: wanattn_partial_fwd_workspace_bytes(B, Lk, H, D, table != NULL).
+ * Workspace: wanattn_partial_fwd_workspace_bytes(B, Lk, H, D, table != NULL):
+ * the key/value tiles only (no tail split).
  * ------------------------------------------------------------------------- */
 size_t wanattn_partial_fwd_workspace_bytes(int B, int Lk, int H, int D, int with_rope);
 
