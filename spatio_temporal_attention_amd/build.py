@@ -17,11 +17,12 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libwanattn.so")
 
 SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
-           "merge.hip", "validate.cpp"]
+           "attn_bwd_dv.hip", "merge.hip", "validate.cpp"]
 # Per-file compiler options.  The self-attention forward's products phase
 # needs the iterative ILP machine scheduler to keep LDS reads ahead of its
 # MFMAs (the default one reads each fragment right before its use there).
-EXTRA_FLAGS = {"attn_fwd_pp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+EXTRA_FLAGS = {"attn_fwd_pp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+               "attn_bwd_dv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = "gfx950"
 
 

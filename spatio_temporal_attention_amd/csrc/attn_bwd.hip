@@ -18,7 +18,7 @@
 // matching the accumulator registers), so no LDS transpose read is needed.
 // The inverse rotation is fused into the dQ and dK stores.
 //
-//  * bwd_dv:   workgroup = 256 keys (8 waves x 32, one workgroup per CU),
+//  * bwd_dv (attn_bwd_dv.hip):   workgroup = 256 keys (8 waves x 32, one workgroup per CU),
 //    loop over 64-query tiles staged as Q fp16 rows and dO^T.  S = Q K^T
 //    (lane owns key j), dV^T += dO^T P with P from the accumulators.
 //  * bwd_dk:   workgroup = 256 keys (8 waves x 32, one workgroup per CU),
@@ -31,253 +31,13 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "common.h"
-#include "kernels.h"
+#include "bwd_common.h"
 
 namespace wanattn {
 
 namespace {
 
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr int DV_WAVES = 8;
-constexpr int DK_WAVES = 8;
-constexpr int DQ_WAVES = 8;
-
-// Store 4 consecutive head-dim elements [d0, d0+4) of token n (two rotary
-// pairs), optionally rotated back by minus the angle, as bf16.
-__device__ __forceinline__ void store_grad4(uint16_t* row_ptr, const RopeDev& rope, const TokenPos& pos, int d0,
-                                            float g0, float g1, float g2, float g3) {
-  if (rope.table != nullptr) {
-    rope_rotate(g0, g1, rope_cs(rope, pos, d0 / 2), true);
-    rope_rotate(g2, g3, rope_cs(rope, pos, d0 / 2 + 1), true);
-  }
-  u32x2 w;
-  w[0] = pack_bf16(g0, g1);
-  w[1] = pack_bf16(g2, g3);
-  *reinterpret_cast<u32x2*>(row_ptr + d0) = w;
-}
-
-// Row `r` of a row tile in global memory as the 8 register fragments of the
-// 32x32x16 operand layout (lane half `half` holds chunks 2s + half).
-__device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* tile, int r, int half, bool ok) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    u32x4 x = u32x4{0u, 0u, 0u, 0u};
-    if (ok) x = *reinterpret_cast<const u32x4*>(tile + r * HD + (2 * s + half) * 8);
-    f[s] = __builtin_bit_cast(bf16x8, x);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dV and dK: one kernel each, so that either fits two waves per SIMD (a wave
-// holding the K and V rows of its keys and both accumulators would need the
-// whole register file: one wave per SIMD, nothing to hide LDS latency or
-// overlap the softmax with the MFMAs).  The scores are recomputed in both.
-// A wave owns 32 keys (lane owns key j); the loop runs over 64-query tiles.
-// KMASK: keys j >= k_lens[b] get P = 0 (cross-attention key padding).
-// ---------------------------------------------------------------------------
-
-// Per-wave key setup shared by both kernels.
-struct KeySide {
-  int b, h, nt, j;
-  int split, t0, t1;   // this workgroup's share [t0, t1) of the query tiles
-  int64_t tile0;     // first query tile of (b, h)
-  int64_t ktile0;    // first key tile of (b, h)
-  int ktile;         // key tile holding this wave's keys
-  bool key_ok, key_live, tile_ok;
-};
-
-template <int NW, bool KMASK>
-__device__ __forceinline__ KeySide key_side(const BwdParams& p, int wave, int col) {
-  KeySide k;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = logical % p.n_tiles;
-  const int rest = logical / p.n_tiles;
-  k.split = rest % p.q_split;
-  const int bh = rest / p.q_split;
-  k.b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
-  k.h = bh / p.B;
-  k.nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;
-  const int chunk = (k.nt + p.q_split - 1) / p.q_split;
-  k.t0 = k.split * chunk;
-  k.t1 = min(k.nt, k.t0 + chunk);
-  const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;
-  k.tile0 = (int64_t)(k.b * p.H + k.h) * k.nt;
-  k.ktile0 = (int64_t)(k.b * p.H + k.h) * ntk;
-  // wave w: row 32*(w%2) + col of key tile (32 NW kb + 32 w) / 64
-  k.ktile = (NW / 2) * kb + (wave >> 1);
-  k.j = kb * 32 * NW + wave * 32 + col;
-  k.key_ok = k.j < p.Lk;
-  k.key_live = !KMASK || k.j < min(max(p.k_lens[k.b], 0), p.Lk);
-  k.tile_ok = k.ktile < ntk;
-  return k;
-}
-
-// dV_j = sum_i P_ij dO_i.  Workgroup = 256 keys (8 waves, one workgroup per
-// CU: each query tile crosses from L2 once per CU, not once per 128 keys);
-// query tiles staged as Q fp16 rows and dO^T.  S = Q K^T from the
-// wave's K rows in registers, dV^T += dO^T P with P from the accumulators.
-template <bool KMASK>
-__global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
-  // Double-buffered tiles as separate objects, named statically in the
-  // two-way unrolled loop (LDS reads do not wait for copies in flight).
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse2_s0[TILE_ROWS];   // LSE * log2 e (+inf: no row)
-  __shared__ __attribute__((aligned(16))) float lse2_s1[TILE_ROWS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int half = lane >> 5;
-  const int col = lane & 31;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const KeySide ks = key_side<DV_WAVES, KMASK>(p, wv, col);
-
-  bf16x8 kf[8];   // K fp16 (bit patterns): B operand of S
-  load_row_frags(kf, p.kf + (ks.ktile0 + (ks.tile_ok ? ks.ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half,
-                 ks.tile_ok);
-  const int e_k = ks.tile_ok ? p.kexp[ks.ktile0 + ks.ktile] : 0;
-
-  f32x16 dv_acc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) dv_acc[d] = f32x16{};
-  const float* lse_row = p.lse + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
-
-  constexpr int NCP = 16 / DV_WAVES;   // 1 KB copies per wave and tile
-  uint32_t roff[NCP], toff[NCP];
-#pragma unroll
-  for (int i = 0; i < NCP; ++i) {
-    roff[i] = rowtile_lane_off<DV_WAVES>(wv, i, lane);
-    toff[i] = ttile_lane_off<DV_WAVES>(wv, i, lane);
-  }
-  const uint32_t bytes = (uint32_t)ks.nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
-  const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + ks.tile0 * TILE_ELEMS, bytes);
-  const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + ks.tile0 * TILE_ELEMS, bytes);
-  const_i32* qexp = const_ptr(p.qexp + ks.tile0);   // scalar loads
-
-  struct Buf {
-    uint16_t* q;
-    uint16_t* dOt;
-    float* lse2;
-  };
-  const Buf buf0{q_lds0, dot_lds0, lse2_s0};
-  const Buf buf1{q_lds1, dot_lds1, lse2_s1};
-  auto stage = [&](const Buf& dst, int t) {
-    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
-#pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      buf_dma16(qfr, roff[i], soff, tile_lds_block<DV_WAVES>(dst.q, wv, i));
-      buf_dma16(dotr, toff[i], soff, tile_lds_block<DV_WAVES>(dst.dOt, wv, i));
-    }
-  };
-  // LSE of query tile t: threads 0..63, into a register, published to LDS
-  // once loaded (rows past Lq, and rows with no valid key, get +inf: P = 0).
-  auto load_stats = [&](int t) {
-    float x = -INFINITY;
-    if (tid < TILE_ROWS) {
-      const int i = t * TILE_ROWS + tid;
-      if (i < p.Lq) x = lse_row[i];
-    }
-    return x;
-  };
-  auto store_stats = [&](const Buf& dst, float x) {
-    if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
-  };
-
-  // A query split can be empty (rounding of the split size): it writes zero partials.
-  if (ks.t0 < ks.t1) {
-    int e_q;
-    {
-      const float st = load_stats(ks.t0);
-      stage(buf0, ks.t0);
-      e_q = qexp[ks.t0];
-      wait_vmem();
-      store_stats(buf0, st);
-    }
-    __syncthreads();
-
-    auto iteration = [&](auto parity, int t) {
-      constexpr int P = decltype(parity)::value;
-      const Buf& cur = P ? buf1 : buf0;
-      const Buf& nxt = P ? buf0 : buf1;
-      const bool has_next = t + 1 < ks.t1;
-      int e_q_next = 0;
-      float st = 0.f;
-      if (has_next) {
-        st = load_stats(t + 1);
-        stage(nxt, t + 1);
-        e_q_next = qexp[t + 1];
-      }
-      const float g = ldexpf(p.scale_log2, e_q + e_k);
-      bf16x8 pf[4];
-  #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s_acc = f32x16{};
-  #pragma unroll
-        for (int s = 0; s < 8; ++s) s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-        float pv[16];
-  #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
-            if (KMASK && !ks.key_live) pe = 0.f;
-            pv[4 * m + e] = pe;
-          }
-        }
-        pf[2 * qb] = pack_acc8(pv);
-        pf[2 * qb + 1] = pack_acc8(pv + 8);
-      }
-  #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-  #pragma unroll
-        for (int qg = 0; qg < 4; ++qg) dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
-      }
-      if (has_next) {
-        wait_vmem();
-        store_stats(nxt, st);
-      }
-      __syncthreads();
-      e_q = e_q_next;
-    };
-    int t = ks.t0;
-    for (; t + 1 < ks.t1; t += 2) {
-      iteration(std::integral_constant<int, 0>{}, t);
-      iteration(std::integral_constant<int, 1>{}, t + 1);
-    }
-    if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
-  }
-
-  if (ks.key_ok && p.q_split > 1) {
-    // fp32 partial over this split's query tiles, summed by bwd_kv_reduce_kernel
-    const int64_t part = (int64_t)p.q_split * p.B * p.H * p.Lk * HD;   // dV follows dK~
-    float* row = p.part + part + ((((int64_t)ks.split * p.B + ks.b) * p.H + ks.h) * p.Lk + ks.j) * HD;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq)
-        *reinterpret_cast<f32x4*>(row + d * 32 + 8 * jq + 4 * half) =
-            f32x4{dv_acc[d][4 * jq], dv_acc[d][4 * jq + 1], dv_acc[d][4 * jq + 2], dv_acc[d][4 * jq + 3]};
-    }
-  } else if (ks.key_ok) {
-    uint16_t* dvrow = p.dv + ((int64_t)ks.b * p.Lk * p.H + ks.h) * HD + (int64_t)ks.j * p.H * HD;
-    RopeDev none = p.rope;
-    none.table = nullptr;
-    const TokenPos pos{0, 0, 0};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq)
-        store_grad4(dvrow, none, pos, d * 32 + 8 * jq + 4 * half, dv_acc[d][4 * jq], dv_acc[d][4 * jq + 1],
-                    dv_acc[d][4 * jq + 2], dv_acc[d][4 * jq + 3]);
-    }
-  }
-}
+using namespace bwd;
 
 // dk~_j = scale sum_i dS_ij q~_i, dS_ij = P_ij (<dO_i, v_j> - Delta_i).
 // Workgroup = 256 keys (8 waves, one workgroup per CU); query tiles staged
@@ -650,14 +410,9 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
   if (p.q_split < 1 || (p.q_split > 1 && p.part == nullptr)) return hipErrorInvalidValue;
   BwdParams q = p;
   q.n_tiles = (p.Lk + 32 * DV_WAVES - 1) / (32 * DV_WAVES);
-  int64_t total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
-  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  if (p.k_lens != nullptr)
-    hipLaunchKernelGGL(bwd_dv_kernel<true>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
-  else
-    hipLaunchKernelGGL(bwd_dv_kernel<false>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
+  if (launch_bwd_dv(q, stream) != hipSuccess) return hipErrorInvalidValue;
   q.n_tiles = (p.Lk + 32 * DK_WAVES - 1) / (32 * DK_WAVES);
-  total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
+  int64_t total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   if (p.k_lens != nullptr)
     hipLaunchKernelGGL(bwd_dk_kernel<true>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);

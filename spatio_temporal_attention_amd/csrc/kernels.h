@@ -94,6 +94,8 @@ hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf
 hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
                               uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
                               const RopeDev& rope, hipStream_t stream);
+// The dV pass alone (attn_bwd_dv.hip), p.n_tiles = key blocks of 256; called by launch_bwd_dkdv.
+hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 
