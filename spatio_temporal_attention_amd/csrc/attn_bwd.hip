@@ -150,6 +150,9 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
         stage(nxt, t + 1);
         e_q_next = qexp[t + 1];
       }
+      // With a key mask, a wave whose 32 keys are all padding skips the products
+      // (its gradients stay zero) but still copies its share and meets every barrier.
+      if (!KMASK || ks.wave_live) {
       const float g = ldexpf(p.scale_log2, e_q + e_k);
       bf16x8 dsf[4];
   #pragma unroll
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
       for (int d = 0; d < 4; ++d) {
   #pragma unroll
         for (int qg = 0; qg < 4; ++qg) dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
+      }
       }
       if (has_next) {
         wait_vmem();

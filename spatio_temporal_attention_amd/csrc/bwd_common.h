@@ -57,6 +57,7 @@ struct KeySide {
   int64_t ktile0;    // first key tile of (b, h)
   int ktile;         // key tile holding this wave's keys
   bool key_ok, key_live, tile_ok;
+  bool wave_live;   // some key of this wave's 32 is valid (all are without a key mask)
 };
 
 template <int NW, bool KMASK>
@@ -81,6 +82,7 @@ __device__ __forceinline__ KeySide key_side(const BwdParams& p, int wave, int co
   k.j = kb * 32 * NW + wave * 32 + col;
   k.key_ok = k.j < p.Lk;
   k.key_live = !KMASK || k.j < min(max(p.k_lens[k.b], 0), p.Lk);
+  k.wave_live = !KMASK || kb * 32 * NW + wave * 32 < min(max(p.k_lens[k.b], 0), p.Lk);
   k.tile_ok = k.ktile < ntk;
   return k;
 }
