@@ -251,6 +251,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.scale_log2 = scale * LOG2E_F;
   p.q_split = w.q_split;
   p.part = (float*)(base + w.part);
+  p.dq_part = w.dq_part != 0 ? (float*)(base + w.dq_part) : nullptr;
   int e = hip_status(launch_bwd_k_tiles((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)(base + w.kf),
                                         (int*)(base + w.kexp), (uint16_t*)(base + w.kt), (uint16_t*)(base + w.vr), B,
                                         Lk, H, rope, k_lens, s));

@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "bwd_common.h"
+#include "validate.h"
 
 namespace wanattn {
 
@@ -260,6 +261,8 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup owns 256 queries (query tiles 4qb .. 4qb+3); loop over 64-key tiles.
 // ---------------------------------------------------------------------------
+// SPLIT: the tail launch (one key range of a query block, fp32 partial of dq~ out).
+template <bool SPLIT>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][3][TILE_ELEMS];   // [buf][K fp16 | (Rk)^T | V]
 
@@ -270,7 +273,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  int logical, split = 0;
+  if (SPLIT) {
+    logical = p.dq_base + (int)blockIdx.x / p.dq_split;
+    split = (int)blockIdx.x % p.dq_split;
+  } else {
+    logical = xcd_remap(blockIdx.x, gridDim.x);
+  }
   const int qb = logical % p.n_tiles;
   const int bh = logical / p.n_tiles;
   const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
@@ -280,7 +289,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const int64_t tile0 = (int64_t)(b * p.H + h) * nt;
   const int64_t ktile0 = (int64_t)(b * p.H + h) * ntk;
   const int n_keys = p.k_lens != nullptr ? min(max(p.k_lens[b], 0), p.Lk) : p.Lk;
-  const int nkt = (n_keys + TILE_ROWS - 1) / TILE_ROWS;  // key tiles visited
+  const int nkt = (n_keys + TILE_ROWS - 1) / TILE_ROWS;  // key tiles of valid keys
+  // Key tiles [t0, t1): all of them, or one of p.dq_split ranges.
+  int t0 = 0, t1 = nkt;
+  if (SPLIT) {
+    const int chunk = (nkt + p.dq_split - 1) / p.dq_split;
+    t0 = min(nkt, split * chunk);
+    t1 = min(nkt, t0 + chunk);
+  }
 
   // This lane's query i: row 32*(wave%2) + col of query tile 4qb + wave/2.
   const int qtile = 4 * qb + (wv >> 1);
@@ -323,9 +339,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   };
 
   int e_k = 0;
-  if (nkt > 0) {
-    stage(0, 0);
-    e_k = kexp[0];
+  if (t1 > t0) {
+    stage(0, t0);
+    e_k = kexp[t0];
   }
   wait_vmem();
   __syncthreads();
@@ -368,11 +384,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     }
   };
 
-  // Full tiles in the loop; a partial last tile is peeled off after it.
-  const int n_full = n_keys / TILE_ROWS;
-  for (int t = 0; t < n_full; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < nkt;
+  // Full tiles in the loop; a partial last tile is peeled off after it (only by the range that holds it:
+  // an empty range, t0 == t1 == nkt, has n_full == t1).
+  const int n_full = max(t0, min(n_keys / TILE_ROWS, t1));
+  for (int t = t0; t < n_full; ++t) {
+    const int buf = (t - t0) & 1;
+    const bool has_next = t + 1 < t1;
     int e_k_next = 0;
     if (has_next) {
       stage(buf ^ 1, t + 1);
@@ -383,8 +400,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     e_k = e_k_next;
   }
-  if (n_full < nkt) key_tile(std::true_type{}, n_full, n_full & 1);
+  if (n_full < t1) key_tile(std::true_type{}, n_full, (n_full - t0) & 1);
 
+  if (SPLIT) {
+    // Partial dq~ of this key range (unscaled, unrotated): rows of 128 fp32.
+    float* dst = p.dq_part + ((int64_t)blockIdx.x * 256 + wave * 32 + col) * HD;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<f32x4*>(dst + d * 32 + 8 * jq + 4 * half) =
+            f32x4{dq_acc[d][4 * jq], dq_acc[d][4 * jq + 1], dq_acc[d][4 * jq + 2], dq_acc[d][4 * jq + 3]};
+    return;
+  }
   if (row_ok) {
     TokenPos pos{0, 0, 0};
     if (p.rope.table != nullptr) pos = token_pos(p.rope, i);
@@ -400,6 +428,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       }
     }
   }
+}
+
+// Sum of the dQ tail split's partials (fixed order over the key ranges), then
+// dq = R(p_i)^T scale dq~ in bf16.  One thread per row and four head-dim columns.
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(BwdParams p, int tail) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c4 = (int)(idx & 31);
+  const int64_t rr = idx >> 5;
+  const int rl = (int)(rr % 256);
+  const int ti = (int)(rr / 256);
+  if (ti >= tail) return;
+  const int logical = p.dq_base + ti;
+  const int qb = logical % p.n_tiles;
+  const int bh = logical / p.n_tiles;
+  const int b = bh % p.B;
+  const int h = bh / p.B;
+  const int i = qb * 256 + rl;
+  if (i >= p.Lq) return;
+  const float* src = p.dq_part + ((int64_t)ti * p.dq_split * 256 + rl) * HD + 4 * c4;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.dq_split; ++s) acc += *reinterpret_cast<const f32x4*>(src + (int64_t)s * 256 * HD);
+  TokenPos pos{0, 0, 0};
+  if (p.rope.table != nullptr) pos = token_pos(p.rope, i);
+  uint16_t* dqrow = p.dq + (((int64_t)b * p.Lq + i) * p.H + h) * HD;
+  store_grad4(dqrow, p.rope, pos, 4 * c4, acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
 }
 
 // The tiles of one (b, h) are addressed through buffer resources of 32-bit extent.
@@ -436,7 +489,18 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
   q.n_tiles = (p.Lq + 255) / 256;
   const int64_t total = (int64_t)q.n_tiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)total), dim3(64 * DQ_WAVES), 0, stream, q);
+  // Tail split by the rule the workspace was sized by (256-row query blocks, as the forward's).
+  FwdSplit sp{(int)total, (int)total, 0, 1};
+  if (p.dq_part != nullptr) sp = fwd_tail_split(p.B, p.Lq, p.H);
+  if (sp.n != total) return hipErrorInvalidValue;
+  if (sp.n_main > 0)
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)sp.n_main), dim3(64 * DQ_WAVES), 0, stream, q);
+  if (sp.tail > 0) {
+    q.dq_base = sp.n_main;
+    q.dq_split = sp.S;
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(sp.tail * sp.S)), dim3(64 * DQ_WAVES), 0, stream, q);
+    hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)(sp.tail * 32)), dim3(256), 0, stream, q, sp.tail);
+  }
   return hipGetLastError();
 }
 

@@ -57,6 +57,10 @@ struct BwdParams {
   float scale_log2;
   int q_split;              // dK/dV: query range split over this many workgroups per key block (>= 1)
   float* part;              // q_split > 1: fp32 partial dK~ then dV, [q_split][B][H][Lk][128] each
+  // Tail split of the dQ pass: fp32 partials of dq~ (nullptr: none); dq_base and
+  // dq_split are set by the launcher.
+  float* dq_part;
+  int dq_base, dq_split;
   int n_tiles;              // set by the launchers
 };
 

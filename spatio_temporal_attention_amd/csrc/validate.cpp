@@ -143,6 +143,13 @@ BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
     w.part = align256(at);
     at = w.part + 2 * (size_t)w.q_split * B * H * Lk * (size_t)D * 4;
   }
+  // dQ pass: the last query blocks as key ranges, fp32 partials of dq~ [tail * S][256 rows][D].
+  w.dq_split = fwd_tail_split(B, Lq, H);
+  w.dq_part = 0;
+  if (w.dq_split.tail > 0) {
+    w.dq_part = align256(at);
+    at = w.dq_part + (size_t)w.dq_split.tail * w.dq_split.S * FWD_ROWS * (size_t)D * 4;
+  }
   w.total = at;
   return w;
 }

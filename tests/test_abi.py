@@ -82,9 +82,15 @@ def test_workspace_sizes(lib):
     assert lib.wanattn_self_fwd_workspace_bytes(1, 2048, 130, D, 0) == 2 * 130 * 2048 * D * 2 + 16 * 8 * 256 * 132 * 4
     delta = (B * H * L * 4 + 255) // 256 * 256
     exps = (4 * n_tiles + 255) // 256 * 256 + 4 * n_tiles
-    # Delta, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == delta + 7 * tiled * 2 + exps
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == delta + 7 * tiled * 2 + exps
+    # Delta, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents, then the
+    # dQ pass's tail split (the forward's rule over 256-row query blocks): 64 blocks x 4 key ranges of fp32 rows
+    dq_part = 64 * 4 * 256 * D * 4
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == up(delta + 7 * tiled * 2 + exps) + dq_part
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == up(delta + 7 * tiled * 2 + exps) + dq_part
+    # no tail split: the layout ends with the key tile exponents (32 heads: 37 rounds of 256 blocks)
+    d32, t32 = (B * 32 * L * 4 + 255) // 256 * 256, B * 32 * ((L + 63) // 64)
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, 32, D, 1) == (
+        d32 + 7 * small * 2 + (4 * t32 + 255) // 256 * 256 + 4 * t32)
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, 64, 1) == 0
 
 
@@ -105,7 +111,9 @@ def test_cross_bwd_workspace_with_query_split(lib):
     a256 = lambda x: (x + 255) // 256 * 256
     qt, kt = B * H * ((Lq + 63) // 64), B * H * ((Lk + 63) // 64)
     base = a256(B * H * Lq * 4) + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt
-    assert lib.wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D) == a256(base) + 2 * 7 * B * H * Lk * D * 4
+    # then the dK/dV partials of the 7 query ranges, then the dQ tail split's (64 query blocks x 4 key ranges)
+    assert lib.wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D) == (
+        a256(a256(base) + 2 * 7 * B * H * Lk * D * 4) + 64 * 4 * 256 * D * 4)
     # no split: the layout ends with the key tile exponents
     qt, kt = 2 * 2 * 2, 2 * 2 * 8                      # 64-token tiles over B x H
     assert lib.wanattn_cross_bwd_workspace_bytes(2, 100, 512, 2, D) == (

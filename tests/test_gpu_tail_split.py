@@ -1,11 +1,13 @@
-"""GPU parity of the self-attention forward's tail split against the fp64 oracle.
+"""GPU parity of the tail splits against the fp64 oracle.
 
-The forward runs 256-row query tiles, 256 at a time; when a large problem's
-tile count n is not a multiple of 256, the last n % 256 tiles run as several
-key ranges each whose fp32 partials are merged exactly.  These shapes put the
-split on known heads (logical tile = (head * B + item) * tiles_per_head + qt,
-batch item innermost) and check those heads in full; same bar as the other
-parity tests (max-abs 2e-2, rel-L2 5e-3 on O; |LSE error| 1e-3)."""
+The forward and the backward's dQ pass run 256-row query blocks, 256 at a time;
+when a large problem's block count n is not a multiple of 256, the last n % 256
+blocks run as several key ranges each, whose fp32 partials are combined after
+(the forward merges softmax partials exactly; dQ sums its partials in range
+order).  These shapes put the split on known heads (logical block =
+(head * B + item) * blocks_per_head + qb, batch item innermost) and check those
+heads in full; same bar as the other parity tests (max-abs 2e-2, rel-L2 5e-3 on
+O, dQ, dK, dV; |LSE error| 1e-3)."""
 
 import math
 
@@ -94,3 +96,62 @@ def test_tail_split_varlen_masked_ranges_and_rows():
             check_lse("LSE", gl[b, h, :n], rl[b, j, :n])
             assert np.all(go[b, n:, h] == 7.0), "rows past the length were written"
             assert np.all(gl[b, h, n:] == 5.0), "LSE past the length was written"
+
+
+def test_dq_tail_split_heads_match_oracle():
+    """Self-attention backward with 130 heads at L = 2048: the dQ blocks of heads 128 and 129 run as 8 key
+    ranges of 4 key tiles; their gradients (and one head of the main launch) against the oracle, and the
+    split heads' dQ bit-identical over two calls."""
+    B, H = 1, 130
+    L = int(np.prod(GRID))
+    assert _split_rule(B, L, H) == (1024, 16, 8)
+    q, k, v, do = (synth.random_bf16(9300 + i, (B, L, H, 128)) for i in range(4))
+    table = wa.rope_table(GRID, ROPE)
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = wa.self_fwd(qd, kd, vd, grid=GRID, table=table, rope=ROPE, scale=SCALE)
+    dq, dk, dv = wa.self_bwd(qd, kd, vd, o, lse, dod, grid=GRID, table=table, rope=ROPE, scale=SCALE)
+    dq2 = torch.full_like(dq, 3.0)
+    wa.self_bwd(qd, kd, vd, o, lse, dod, grid=GRID, table=table, rope=ROPE, scale=SCALE, dq=dq2)
+    torch.cuda.synchronize()
+    assert torch.equal(dq.view(torch.int16).cpu(), dq2.view(torch.int16).cpu()), "dQ differs between two calls"
+    gq, gk, gv = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+    heads = [128, 129, 0]
+    f = synth.bf16_bits_to_f64
+    rq, rk, rv = oracle.self_bwd_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), f(do[:, :, heads]),
+                                     SCALE, GRID, ROPE)
+    for j, h in enumerate(heads):
+        print(f"  head {h}:")
+        check_close("dQ", gq[:, :, h], rq[:, :, j])
+        check_close("dK", gk[:, :, h], rk[:, :, j])
+        check_close("dV", gv[:, :, h], rv[:, :, j])
+
+
+def test_dq_tail_split_cross_with_empty_key_ranges():
+    """Cross-attention backward, 2 items x 65 heads x 2048 queries over 512 text tokens, lengths 512 and 100:
+    head 64's dQ blocks run as 8 key ranges; item 1 has 2 key tiles, so 6 of its ranges hold no key and
+    contribute zero partials."""
+    B, Lq, Lk, H = 2, 2048, 512, 65
+    assert _split_rule(B, Lq, H) == (1024, 16, 8)
+    q, do = (synth.random_bf16(9400 + i, (B, Lq, H, 128)) for i in range(2))
+    k, v = (synth.random_bf16(9410 + i, (B, Lk, H, 128)) for i in range(2))
+    lens = np.array([512, 100], dtype=np.int32)
+    nan_bits = np.uint16(0x7FC0)
+    for b, n in enumerate(lens):                   # padded keys hold NaN: never read
+        k[b, n:] = nan_bits
+        v[b, n:] = nan_bits
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    kl = torch.from_numpy(lens).cuda()
+    o, lse = wa.cross_fwd(qd, kd, vd, kl, scale=SCALE)
+    dq, dk, dv = wa.cross_bwd(qd, kd, vd, kl, o, lse, dod, scale=SCALE)
+    torch.cuda.synchronize()
+    gq, gk, gv = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+    heads = [64, 5]                                # the split head, and one of the main launch
+    f = synth.bf16_bits_to_f64
+    rq, rk, rv = oracle.cross_bwd_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), f(do[:, :, heads]),
+                                      lens, SCALE)
+    for j, h in enumerate(heads):
+        for b, n in enumerate(lens):
+            print(f"  head {h}, item {b} (k_len {n}):")
+            check_close("dQ", gq[b, :, h], rq[b, :, j])
+            check_close("dK", gk[b, :n, h], rk[b, :n, j])
+            check_close("dV", gv[b, :n, h], rv[b, :n, j])
