@@ -252,6 +252,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.q_split = w.q_split;
   p.part = (float*)(base + w.part);
   p.dq_part = w.dq_part != 0 ? (float*)(base + w.dq_part) : nullptr;
+  p.kv_part = w.kv_part != 0 ? (float*)(base + w.kv_part) : nullptr;
   int e = hip_status(launch_bwd_k_tiles((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)(base + w.kf),
                                         (int*)(base + w.kexp), (uint16_t*)(base + w.kt), (uint16_t*)(base + w.vr), B,
                                         Lk, H, rope, k_lens, s));

@@ -45,7 +45,7 @@ using namespace bwd;
 // as Q fp16 rows, dO rows and (R q)^T.  S = Q K^T and dP - Delta = dO V^T -
 // Delta (the accumulator starts at -Delta of its rows) from the wave's K
 // and V rows in registers; dK~^T += (R q)^T dS with dS from the accumulators.
-template <bool KMASK>
+template <bool KMASK, bool TAIL>
 __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const KeySide ks = key_side<DK_WAVES, KMASK>(p, wv, col);
+  const KeySide ks = key_side<DK_WAVES, KMASK, TAIL>(p, wv, col);
 
   bf16x8 kf[8], vf[8];   // K fp16 (bit patterns), V bf16: B operands of S and dP
   const int64_t ktile = ks.ktile0 + (ks.tile_ok ? ks.ktile : 0);
@@ -206,7 +206,17 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
     if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
   }
 
-  if (ks.key_ok && p.q_split > 1) {
+  if (TAIL) {
+    // fp32 partial (unscaled, unrotated) over this query range, rows of the workgroup's 256 keys
+    float* row = p.kv_part + ((int64_t)blockIdx.x * (32 * DK_WAVES) + wave * 32 + col) * HD;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<f32x4*>(row + d * 32 + 8 * jq + 4 * half) =
+            f32x4{dk_acc[d][4 * jq], dk_acc[d][4 * jq + 1], dk_acc[d][4 * jq + 2], dk_acc[d][4 * jq + 3]};
+    }
+  } else if (ks.key_ok && p.q_split > 1) {
     // fp32 partial (unscaled, unrotated) over this split's query tiles
     float* row = p.part + ((((int64_t)ks.split * p.B + ks.b) * p.H + ks.h) * p.Lk + ks.j) * HD;
 #pragma unroll
@@ -256,6 +266,38 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p) {
     store_grad4(p.dk + off, p.rope, pos, d0, sk[0] * p.scale, sk[1] * p.scale, sk[2] * p.scale, sk[3] * p.scale);
     store_grad4(p.dv + off, none, pos, d0, sv[0], sv[1], sv[2], sv[3]);
   }
+}
+
+// Sum of the dK/dV tail split's partials (fixed order over the query ranges), then
+// dk = R(p_j)^T scale dK~ and dv in bf16.  One thread per key and four head-dim columns.
+__global__ __launch_bounds__(256) void bwd_kv_tail_reduce_kernel(BwdParams p, int tail) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c4 = (int)(idx & 31);
+  const int64_t rr = idx >> 5;
+  const int rl = (int)(rr % 256);
+  const int ti = (int)(rr / 256);
+  if (ti >= tail) return;
+  const int logical = p.kv_base + ti;
+  const int kb = logical % p.n_tiles;
+  const int bh = logical / p.n_tiles;
+  const int b = bh % p.B;
+  const int h = bh / p.B;
+  const int j = kb * 256 + rl;
+  if (j >= p.Lk) return;
+  const int64_t region = (int64_t)tail * p.kv_split * 256 * HD;   // dV partials follow dK~
+  const float* src = p.kv_part + ((int64_t)ti * p.kv_split * 256 + rl) * HD + 4 * c4;
+  f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.kv_split; ++s) {
+    sk += *reinterpret_cast<const f32x4*>(src + (int64_t)s * 256 * HD);
+    sv += *reinterpret_cast<const f32x4*>(src + region + (int64_t)s * 256 * HD);
+  }
+  TokenPos pos{0, 0, 0};
+  if (p.rope.table != nullptr) pos = token_pos(p.rope, j);
+  RopeDev none = p.rope;
+  none.table = nullptr;
+  const int64_t off = (((int64_t)b * p.Lk + j) * p.H + h) * HD;
+  store_grad4(p.dk + off, p.rope, pos, 4 * c4, sk[0] * p.scale, sk[1] * p.scale, sk[2] * p.scale, sk[3] * p.scale);
+  store_grad4(p.dv + off, none, pos, 4 * c4, sv[0], sv[1], sv[2], sv[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -465,16 +507,35 @@ bool tiles_addressable(int L) {
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream) {
   if (!tiles_addressable(p.Lq) || !tiles_addressable(p.Lk)) return hipErrorInvalidValue;
   if (p.q_split < 1 || (p.q_split > 1 && p.part == nullptr)) return hipErrorInvalidValue;
+  static_assert(32 * DK_WAVES == 256 && 32 * DV_WAVES == 256, "key blocks of 256 (the tail split's rows)");
   BwdParams q = p;
-  q.n_tiles = (p.Lk + 32 * DV_WAVES - 1) / (32 * DV_WAVES);
-  if (launch_bwd_dv(q, stream) != hipSuccess) return hipErrorInvalidValue;
-  q.n_tiles = (p.Lk + 32 * DK_WAVES - 1) / (32 * DK_WAVES);
-  int64_t total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
+  q.n_tiles = (p.Lk + 255) / 256;
+  const int64_t total = (int64_t)q.n_tiles * p.q_split * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  if (p.k_lens != nullptr)
-    hipLaunchKernelGGL(bwd_dk_kernel<true>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);
-  else
-    hipLaunchKernelGGL(bwd_dk_kernel<false>, dim3((unsigned)total), dim3(64 * DK_WAVES), 0, stream, q);
+  // Tail split by the rule the workspace was sized by (no query split only).
+  FwdSplit sp{(int)total, (int)total, 0, 1};
+  if (p.kv_part != nullptr) {
+    if (p.q_split != 1) return hipErrorInvalidValue;
+    sp = fwd_tail_split(p.B, p.Lk, p.H);
+  }
+  if (sp.n != total) return hipErrorInvalidValue;
+  q.kv_base = sp.n_main;
+  q.kv_split = sp.S;
+  if (launch_bwd_dv(q, sp.n_main, sp.tail * sp.S, stream) != hipSuccess) return hipErrorInvalidValue;
+  if (sp.n_main > 0) {
+    if (p.k_lens != nullptr)
+      hipLaunchKernelGGL((bwd_dk_kernel<true, false>), dim3((unsigned)sp.n_main), dim3(64 * DK_WAVES), 0, stream, q);
+    else
+      hipLaunchKernelGGL((bwd_dk_kernel<false, false>), dim3((unsigned)sp.n_main), dim3(64 * DK_WAVES), 0, stream, q);
+  }
+  if (sp.tail > 0) {
+    const dim3 g((unsigned)(sp.tail * sp.S));
+    if (p.k_lens != nullptr)
+      hipLaunchKernelGGL((bwd_dk_kernel<true, true>), g, dim3(64 * DK_WAVES), 0, stream, q);
+    else
+      hipLaunchKernelGGL((bwd_dk_kernel<false, true>), g, dim3(64 * DK_WAVES), 0, stream, q);
+    hipLaunchKernelGGL(bwd_kv_tail_reduce_kernel, dim3((unsigned)(sp.tail * 32)), dim3(256), 0, stream, q, sp.tail);
+  }
   if (p.q_split > 1) {
     const int64_t n4 = (int64_t)p.B * p.H * p.Lk * (HD / 4);
     const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 65536);

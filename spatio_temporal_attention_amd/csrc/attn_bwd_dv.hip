@@ -18,7 +18,7 @@ using namespace bwd;
 // CU: each query tile crosses from L2 once per CU, not once per 128 keys);
 // query tiles staged as Q fp16 rows and dO^T.  S = Q K^T from the
 // wave's K rows in registers, dV^T += dO^T P with P from the accumulators.
-template <bool KMASK>
+template <bool KMASK, bool TAIL>
 __global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
   // Double-buffered tiles as separate objects, named statically in the
   // two-way unrolled loop (LDS reads do not wait for copies in flight).
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const KeySide ks = key_side<DV_WAVES, KMASK>(p, wv, col);
+  const KeySide ks = key_side<DV_WAVES, KMASK, TAIL>(p, wv, col);
 
   bf16x8 kf[8];   // K fp16 (bit patterns): B operand of S
   load_row_frags(kf, p.kf + (ks.ktile0 + (ks.tile_ok ? ks.ktile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half,
@@ -154,7 +154,18 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
     if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
   }
 
-  if (ks.key_ok && p.q_split > 1) {
+  if (TAIL) {
+    // fp32 partial over this query range, rows of the workgroup's 256 keys, after the dK~ partials
+    const int64_t region = (int64_t)gridDim.x * (32 * DV_WAVES) * HD;
+    float* row = p.kv_part + region + ((int64_t)blockIdx.x * (32 * DV_WAVES) + wave * 32 + col) * HD;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<f32x4*>(row + d * 32 + 8 * jq + 4 * half) =
+            f32x4{dv_acc[d][4 * jq], dv_acc[d][4 * jq + 1], dv_acc[d][4 * jq + 2], dv_acc[d][4 * jq + 3]};
+    }
+  } else if (ks.key_ok && p.q_split > 1) {
     // fp32 partial over this split's query tiles, summed by bwd_kv_reduce_kernel
     const int64_t part = (int64_t)p.q_split * p.B * p.H * p.Lk * HD;   // dV follows dK~
     float* row = p.part + part + ((((int64_t)ks.split * p.B + ks.b) * p.H + ks.h) * p.Lk + ks.j) * HD;
@@ -182,14 +193,23 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
 
 }  // namespace
 
-hipError_t launch_bwd_dv(const BwdParams& q, hipStream_t stream) {
-  // q.n_tiles: key blocks of 32 * DV_WAVES keys; the grid is blocks x q_split x H x B.
+hipError_t launch_bwd_dv(const BwdParams& q, int n_main, int n_tail, hipStream_t stream) {
+  // q.n_tiles: key blocks of 32 * DV_WAVES keys; the main grid is blocks x q_split x H x B less the
+  // tail's blocks, which run as n_tail = tail x kv_split workgroups.
   const int64_t total = (int64_t)q.n_tiles * q.q_split * q.H * q.B;
-  if (total <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
-  if (q.k_lens != nullptr)
-    hipLaunchKernelGGL(bwd_dv_kernel<true>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
-  else
-    hipLaunchKernelGGL(bwd_dv_kernel<false>, dim3((unsigned)total), dim3(64 * DV_WAVES), 0, stream, q);
+  if (total <= 0 || total > 0x7fffffff || n_main < 0 || n_tail < 0) return hipErrorInvalidValue;
+  if (n_main > 0) {
+    if (q.k_lens != nullptr)
+      hipLaunchKernelGGL((bwd_dv_kernel<true, false>), dim3((unsigned)n_main), dim3(64 * DV_WAVES), 0, stream, q);
+    else
+      hipLaunchKernelGGL((bwd_dv_kernel<false, false>), dim3((unsigned)n_main), dim3(64 * DV_WAVES), 0, stream, q);
+  }
+  if (n_tail > 0) {
+    if (q.k_lens != nullptr)
+      hipLaunchKernelGGL((bwd_dv_kernel<true, true>), dim3((unsigned)n_tail), dim3(64 * DV_WAVES), 0, stream, q);
+    else
+      hipLaunchKernelGGL((bwd_dv_kernel<false, true>), dim3((unsigned)n_tail), dim3(64 * DV_WAVES), 0, stream, q);
+  }
   return hipSuccess;
 }
 

@@ -60,19 +60,31 @@ struct KeySide {
   bool wave_live;   // some key of this wave's 32 is valid (all are without a key mask)
 };
 
-template <int NW, bool KMASK>
+// TAIL: the tail launch of a pass without a query split; workgroup x is query range
+// x % kv_split of key block kv_base + x / kv_split.
+template <int NW, bool KMASK, bool TAIL>
 __device__ __forceinline__ KeySide key_side(const BwdParams& p, int wave, int col) {
   KeySide k;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kb = logical % p.n_tiles;
-  const int rest = logical / p.n_tiles;
-  k.split = rest % p.q_split;
-  const int bh = rest / p.q_split;
+  int kb, bh, n_split;
+  if (TAIL) {
+    const int logical = p.kv_base + (int)blockIdx.x / p.kv_split;
+    k.split = (int)blockIdx.x % p.kv_split;
+    n_split = p.kv_split;
+    kb = logical % p.n_tiles;
+    bh = logical / p.n_tiles;
+  } else {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    kb = logical % p.n_tiles;
+    const int rest = logical / p.n_tiles;
+    k.split = rest % p.q_split;
+    n_split = p.q_split;
+    bh = rest / p.q_split;
+  }
   k.b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
   k.h = bh / p.B;
   k.nt = (p.Lq + TILE_ROWS - 1) / TILE_ROWS;
-  const int chunk = (k.nt + p.q_split - 1) / p.q_split;
-  k.t0 = k.split * chunk;
+  const int chunk = (k.nt + n_split - 1) / n_split;
+  k.t0 = min(k.nt, k.split * chunk);
   k.t1 = min(k.nt, k.t0 + chunk);
   const int ntk = (p.Lk + TILE_ROWS - 1) / TILE_ROWS;
   k.tile0 = (int64_t)(k.b * p.H + k.h) * k.nt;

@@ -61,6 +61,10 @@ struct BwdParams {
   // dq_split are set by the launcher.
   float* dq_part;
   int dq_base, dq_split;
+  // Tail split of the dK/dV passes (q_split == 1 only): fp32 partials of dK~ then dV (nullptr: none);
+  // kv_base and kv_split are set by the launcher.
+  float* kv_part;
+  int kv_base, kv_split;
   int n_tiles;              // set by the launchers
 };
 
@@ -98,8 +102,9 @@ hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf
 hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
                               uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
                               const RopeDev& rope, hipStream_t stream);
-// The dV pass alone (attn_bwd_dv.hip), p.n_tiles = key blocks of 256; called by launch_bwd_dkdv.
-hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t stream);
+// The dV pass alone (attn_bwd_dv.hip), p.n_tiles = key blocks of 256; called by launch_bwd_dkdv
+// with the workgroup counts of the main launch and of the tail split's launch (0: none).
+hipError_t launch_bwd_dv(const BwdParams& p, int n_main, int n_tail, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 

@@ -143,6 +143,15 @@ BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
     w.part = align256(at);
     at = w.part + 2 * (size_t)w.q_split * B * H * Lk * (size_t)D * 4;
   }
+  // dK/dV passes without a query split: the last key blocks as query ranges, fp32 partials of dK~ then
+  // dV, [tail * S][256 keys][D] each.
+  w.kv_split = FwdSplit{0, 0, 0, 1};
+  if (w.q_split == 1) w.kv_split = fwd_tail_split(B, Lk, H);
+  w.kv_part = 0;
+  if (w.kv_split.tail > 0) {
+    w.kv_part = align256(at);
+    at = w.kv_part + 2 * (size_t)w.kv_split.tail * w.kv_split.S * FWD_ROWS * (size_t)D * 4;
+  }
   // dQ pass: the last query blocks as key ranges, fp32 partials of dq~ [tail * S][256 rows][D].
   w.dq_split = fwd_tail_split(B, Lq, H);
   w.dq_part = 0;

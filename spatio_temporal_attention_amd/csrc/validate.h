@@ -61,8 +61,9 @@ Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D);
 // fp32 partials (2 x q_split x [B, H, Lk, D]); each part starts on a 256-byte
 // boundary.
 struct BwdWsLayout {
-  size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, part, dq_part, total;
+  size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, part, kv_part, dq_part, total;
   int q_split;
+  FwdSplit kv_split;   // tail split of the dK/dV passes (256-key blocks; only without a query split)
   FwdSplit dq_split;   // tail split of the dQ pass (256-row query blocks, the forward's rule)
 };
 // Query-side parts (Delta, qf, qt, dor, dot, qexp) over Lq tokens, key-side

@@ -83,10 +83,11 @@ def test_workspace_sizes(lib):
     delta = (B * H * L * 4 + 255) // 256 * 256
     exps = (4 * n_tiles + 255) // 256 * 256 + 4 * n_tiles
     # Delta, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents, then the
-    # dQ pass's tail split (the forward's rule over 256-row query blocks): 64 blocks x 4 key ranges of fp32 rows
-    dq_part = 64 * 4 * 256 * D * 4
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == up(delta + 7 * tiled * 2 + exps) + dq_part
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == up(delta + 7 * tiled * 2 + exps) + dq_part
+    # tail splits (the forward's rule over blocks of 256 keys or queries): the dK/dV passes' fp32 partials
+    # of dK~ and dV (64 key blocks x 4 query ranges each), then the dQ pass's (64 query blocks x 4 key ranges)
+    kv_part, dq_part = 2 * 64 * 4 * 256 * D * 4, 64 * 4 * 256 * D * 4
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == up(delta + 7 * tiled * 2 + exps) + kv_part + dq_part
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == up(delta + 7 * tiled * 2 + exps) + kv_part + dq_part
     # no tail split: the layout ends with the key tile exponents (32 heads: 37 rounds of 256 blocks)
     d32, t32 = (B * 32 * L * 4 + 255) // 256 * 256, B * 32 * ((L + 63) // 64)
     assert lib.wanattn_self_bwd_workspace_bytes(B, L, 32, D, 1) == (
@@ -111,7 +112,8 @@ def test_cross_bwd_workspace_with_query_split(lib):
     a256 = lambda x: (x + 255) // 256 * 256
     qt, kt = B * H * ((Lq + 63) // 64), B * H * ((Lk + 63) // 64)
     base = a256(B * H * Lq * 4) + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt
-    # then the dK/dV partials of the 7 query ranges, then the dQ tail split's (64 query blocks x 4 key ranges)
+    # then the dK/dV partials of the 7 query ranges (no dK/dV tail split with a query split), then the dQ
+    # tail split's (64 query blocks x 4 key ranges)
     assert lib.wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D) == (
         a256(a256(base) + 2 * 7 * B * H * Lk * D * 4) + 64 * 4 * 256 * D * 4)
     # no split: the layout ends with the key tile exponents

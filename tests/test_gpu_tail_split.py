@@ -1,13 +1,14 @@
 """GPU parity of the tail splits against the fp64 oracle.
 
-The forward and the backward's dQ pass run 256-row query blocks, 256 at a time;
-when a large problem's block count n is not a multiple of 256, the last n % 256
-blocks run as several key ranges each, whose fp32 partials are combined after
-(the forward merges softmax partials exactly; dQ sums its partials in range
-order).  These shapes put the split on known heads (logical block =
-(head * B + item) * blocks_per_head + qb, batch item innermost) and check those
-heads in full; same bar as the other parity tests (max-abs 2e-2, rel-L2 5e-3 on
-O, dQ, dK, dV; |LSE error| 1e-3)."""
+The forward and the backward's dQ pass run 256-row query blocks, the dK/dV
+passes 256-key blocks, 256 at a time; when a large problem's block count n is
+not a multiple of 256, the last n % 256 blocks run as several key (or query)
+ranges each, whose fp32 partials are combined after (the forward merges softmax
+partials exactly; the backward sums its partials in range order).  These shapes
+put the split on known heads (logical block = (head * B + item) *
+blocks_per_head + block, batch item innermost) and check those heads in full;
+same bar as the other parity tests (max-abs 2e-2, rel-L2 5e-3 on O, dQ, dK, dV;
+|LSE error| 1e-3)."""
 
 import math
 
@@ -100,8 +101,8 @@ def test_tail_split_varlen_masked_ranges_and_rows():
 
 def test_dq_tail_split_heads_match_oracle():
     """Self-attention backward with 130 heads at L = 2048: the dQ blocks of heads 128 and 129 run as 8 key
-    ranges of 4 key tiles; their gradients (and one head of the main launch) against the oracle, and the
-    split heads' dQ bit-identical over two calls."""
+    ranges of 4 key tiles, their dK/dV blocks as 8 query ranges of 4 query tiles; their gradients (and one
+    head of the main launch) against the oracle, and all gradients bit-identical over two calls."""
     B, H = 1, 130
     L = int(np.prod(GRID))
     assert _split_rule(B, L, H) == (1024, 16, 8)
@@ -110,10 +111,12 @@ def test_dq_tail_split_heads_match_oracle():
     qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
     o, lse = wa.self_fwd(qd, kd, vd, grid=GRID, table=table, rope=ROPE, scale=SCALE)
     dq, dk, dv = wa.self_bwd(qd, kd, vd, o, lse, dod, grid=GRID, table=table, rope=ROPE, scale=SCALE)
-    dq2 = torch.full_like(dq, 3.0)
-    wa.self_bwd(qd, kd, vd, o, lse, dod, grid=GRID, table=table, rope=ROPE, scale=SCALE, dq=dq2)
+    again = [torch.full_like(dq, 3.0) for _ in range(3)]
+    wa.self_bwd(qd, kd, vd, o, lse, dod, grid=GRID, table=table, rope=ROPE, scale=SCALE, dq=again[0], dk=again[1],
+                dv=again[2])
     torch.cuda.synchronize()
-    assert torch.equal(dq.view(torch.int16).cpu(), dq2.view(torch.int16).cpu()), "dQ differs between two calls"
+    for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), again):
+        assert torch.equal(a.view(torch.int16).cpu(), b.view(torch.int16).cpu()), f"{name} differs between two calls"
     gq, gk, gv = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
     heads = [128, 129, 0]
     f = synth.bf16_bits_to_f64
@@ -155,3 +158,35 @@ def test_dq_tail_split_cross_with_empty_key_ranges():
             check_close("dQ", gq[b, :, h], rq[b, :, j])
             check_close("dK", gk[b, :n, h], rk[b, :n, j])
             check_close("dV", gv[b, :n, h], rv[b, :n, j])
+
+
+def test_kv_tail_split_cross_with_empty_query_ranges():
+    """Cross-attention backward, 2 items x 65 heads x 300 queries over 2048 keys, lengths 2048 and 1500:
+    1,040 key blocks of 256 with no query split, so head 64's key blocks run as 8 query ranges over 5 query
+    tiles (3 of them empty, zero partials); item 1's keys past 1500 are masked and get zero gradients."""
+    B, Lq, Lk, H = 2, 300, 2048, 65
+    assert _split_rule(B, Lk, H) == (1024, 16, 8)
+    q, do = (synth.random_bf16(9500 + i, (B, Lq, H, 128)) for i in range(2))
+    k, v = (synth.random_bf16(9510 + i, (B, Lk, H, 128)) for i in range(2))
+    lens = np.array([2048, 1500], dtype=np.int32)
+    nan_bits = np.uint16(0x7FC0)
+    for b, n in enumerate(lens):                   # padded keys hold NaN: never read
+        k[b, n:] = nan_bits
+        v[b, n:] = nan_bits
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    kl = torch.from_numpy(lens).cuda()
+    o, lse = wa.cross_fwd(qd, kd, vd, kl, scale=SCALE)
+    dq, dk, dv = wa.cross_bwd(qd, kd, vd, kl, o, lse, dod, scale=SCALE)
+    torch.cuda.synchronize()
+    gq, gk, gv = bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)
+    heads = [64, 7]                                # the split head, and one of the main launch
+    f = synth.bf16_bits_to_f64
+    rq, rk, rv = oracle.cross_bwd_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), f(do[:, :, heads]),
+                                      lens, SCALE)
+    for j, h in enumerate(heads):
+        for b, n in enumerate(lens):
+            print(f"  head {h}, item {b} (k_len {n}):")
+            check_close("dQ", gq[b, :, h], rq[b, :, j])
+            check_close("dK", gk[b, :n, h], rk[b, :n, j])
+            check_close("dV", gv[b, :n, h], rv[b, :n, j])
+            assert np.all(gk[b, n:, h] == 0) and np.all(gv[b, n:, h] == 0), "padded keys got a gradient"
