@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_720p_hbm_traffic.json")
+# Query rows per head the oracle computes for the CPU baseline (~15 s of fp64 work on 16 threads).
+CPU_SAMPLE_ROWS = 128
 FWD_SOURCES = ("attn_fwd_pp.hip", "common.h", "kernels.h", "validate.h", "validate.cpp")
 
 
@@ -65,7 +67,7 @@ def log(msg):
 
 
 def cpu_baseline(inp, w, rope, scale):
-    """The fp64 oracle on a bounded sample: 64 seeded query rows of every head."""
+    """The fp64 oracle on a bounded sample: CPU_SAMPLE_ROWS seeded query rows of every head."""
     import numpy as np
     import oracle
     import synth
@@ -209,7 +211,7 @@ def main():
     rope = wa.RopeConfig(48, 40, 40, 10000.0)
     scale = 1.0 / math.sqrt(D)
     t0 = time.perf_counter()
-    inp = synth.make_inputs(4)
+    inp = synth.make_inputs(4, rows_per_head=CPU_SAMPLE_ROWS)
     ctx = synth.make_text_context(4, B, H)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
 
