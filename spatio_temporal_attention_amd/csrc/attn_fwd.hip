@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256, 2) void cross_fwd_kernel(FwdParams p) {
   int n_q = p.Lq;
   if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
   const bool row_ok = i < n_q;
+  if (qt * FWD_BR >= n_q) return;   // query tile wholly past its item's length: nothing to do
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {

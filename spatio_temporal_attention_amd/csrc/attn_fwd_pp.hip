@@ -71,7 +71,10 @@ constexpr int PP_BR = 32 * PP_WAVES;   // query rows per workgroup
 static_assert(PP_BR == FWD_ROWS, "the tail split and its workspace assume 256-row workgroups");
 
 // SPLIT: the tail launch (one key range of a query tile, fp32 partial out).
-template <bool POS_SCALE, bool F16, bool SPLIT>
+// VARLEN: the main launch with variable lengths, where a workgroup whose query
+// tile lies wholly past its item's length leaves at once (an instantiation of
+// its own, so the fixed-length code is unaffected).
+template <bool POS_SCALE, bool F16, bool SPLIT, bool VARLEN>
 // Two waves per SIMD by design (one workgroup per CU); without the explicit
 // target the compiler aims for four (the LDS would allow two workgroups) and
 // schedules for register pressure instead of latency.
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   int n_q = p.Lq;
   if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
   const bool row_ok = i < n_q;
+  if (VARLEN && qt * PP_BR >= n_q) return;   // before the first barrier; nothing to compute or store
   bf16x8 qf[8];
   float g_q = p.scale_log2;
   {
@@ -471,12 +475,20 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
   const dim3 block(64 * PP_WAVES);
   if (sp.n_main > 0) {
     const dim3 grid((unsigned)sp.n_main);
-    if (pos) {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false>), grid, block, 0, stream, r);
+    if (p.q_lens != nullptr) {
+      if (pos) {
+        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, true>), grid, block, 0, stream, r);
+        else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, true>), grid, block, 0, stream, r);
+      } else {
+        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, true>), grid, block, 0, stream, r);
+        else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, true>), grid, block, 0, stream, r);
+      }
+    } else if (pos) {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, false>), grid, block, 0, stream, r);
     } else {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false>), grid, block, 0, stream, r);
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, false>), grid, block, 0, stream, r);
     }
   }
   if (sp.tail > 0) {
@@ -484,11 +496,11 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
     r.n_split = sp.S;
     const dim3 grid((unsigned)(sp.tail * sp.S));
     if (pos) {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, true>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, true>), grid, block, 0, stream, r);
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, true, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, true, false>), grid, block, 0, stream, r);
     } else {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, true>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, true>), grid, block, 0, stream, r);
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, true, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, true, false>), grid, block, 0, stream, r);
     }
     hipLaunchKernelGGL(fwd_split_merge_kernel, dim3((unsigned)(sp.tail * (PP_BR * 32 / 256))), dim3(256), 0, stream,
                        r, sp.tail);
