@@ -181,7 +181,13 @@ int wanattn_self_fwd_fp8(const void* q, const void* k, const void* v, void* o, f
  * forward multiplied; when few key blocks would leave the GPU idle (a short
  * key side: fewer than 256 blocks of 256 keys over B and H), the dK/dV passes
  * split the query range and the workspace also holds their fp32 partial sums
- * (reduced in a fixed order: results stay deterministic).  Its contents on
+ * (reduced in a fixed order: results stay deterministic).  Each pass runs
+ * blocks of 256 keys (dK, dV) or 256 queries (dQ), 256 at a time; for a block
+ * count n that the forward's rule above would split (n >= 1024, t = n % 256,
+ * S = min(8, 256/t) >= 2), the last t blocks run as S ranges of the other
+ * side, and the workspace holds their fp32 partials too ([t*S][256][D] for
+ * dK and for dV when the dK/dV passes have no query split of their own, then
+ * [t*S][256][D] for dQ), also summed in a fixed order.  Its contents on
  * return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_bwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
@@ -274,7 +280,8 @@ int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t
  * Workspace (required, 16-byte aligned): wanattn_cross_bwd_workspace_bytes
  * (the self-attention backward's layout over Lq query and Lk key tokens,
  * including the partial sums of a split query range: at the 720p text shape,
- * B = 1, Lq = 75,600, Lk = 512, H = 40, the query range is split 7 ways).
+ * B = 1, Lq = 75,600, Lk = 512, H = 40, the query range is split 7 ways, and
+ * the tail split's partials of the dQ pass).
  * ------------------------------------------------------------------------- */
 size_t wanattn_cross_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int D);
 
