@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_720p_hbm_traffic.json")
-# Query rows per head the oracle computes for the CPU baseline (~15 s of fp64 work on 16 host threads).
+# Query rows per head the oracle computes for the CPU baseline (about 10-17 s of fp64 work on 16 host threads).
 CPU_SAMPLE_ROWS = 256
 FWD_SOURCES = ("attn_fwd_pp.hip", "common.h", "kernels.h", "validate.h", "validate.cpp")
 

@@ -298,12 +298,19 @@ def test_self_bwd_single_token():
     check_close("dV", dv, _f64(dob))
 
 
-def test_self_bwd_720p_sampled():
+@pytest.fixture(scope="module")
+def bwd_720p():
+    """The 720p workload's inputs and GPU gradients, shared by the tests below."""
     w = synth.WORKLOADS[4]
     inp = synth.make_inputs(4)
     print("  720p: generated", flush=True)
     dq, dk, dv = _run_self_bwd(inp["q"], inp["k"], inp["v"], inp["dout"], w.grid, True)
     print("  720p: GPU done", flush=True)
+    return w, inp, dq, dk, dv
+
+
+def test_self_bwd_720p_sampled(bwd_720p):
+    w, inp, dq, dk, dv = bwd_720p
     rows = inp["rows"]
     got, ref = [], []
     for h in range(w.H):
@@ -320,3 +327,24 @@ def test_self_bwd_720p_sampled():
                                        _f64(inp["dout"][sl]), SCALE, w.grid, ROPE, rows[:, h:h + 1], block=1024)
     check_close(f"dK (sampled, head {h})", dk[0, rows[0, h], h], rk[0, 0])
     check_close(f"dV (sampled, head {h})", dv[0, rows[0, h], h], rv[0, 0])
+
+
+def test_self_bwd_720p_tail_split_keys(bwd_720p):
+    """dK and dV of head 39 at 720p, mostly on keys of its last 64 blocks of 256 (keys 59,392 .. 75,599): 40 heads
+    give 11,840 key blocks, 46 rounds of 256 and 64 left over, which the dK/dV passes run as 4 query ranges each
+    (head 39's dQ rows were sampled with every head above, its last 64 query blocks being the dQ pass's tail)."""
+    w, inp, dq, dk, dv = bwd_720p
+    blocks_per_head = (w.L + 255) // 256
+    n = w.H * blocks_per_head
+    tail = n % 256
+    assert (blocks_per_head, n, tail) == (296, 11840, 64)
+    first_tail_key = (blocks_per_head - tail) * 256
+    assert first_tail_key == 59392
+    h = 39
+    keys = np.unique(np.concatenate([first_tail_key + synth.sample_rows(405, w.L - first_tail_key, 24),
+                                     synth.sample_rows(406, first_tail_key, 8), [first_tail_key, w.L - 1]]))
+    sl = (slice(0, 1), slice(None), slice(h, h + 1))
+    rk, rv = oracle.self_bwd_dkdv_rows(_f64(inp["q"][sl]), _f64(inp["k"][sl]), _f64(inp["v"][sl]),
+                                       _f64(inp["dout"][sl]), SCALE, w.grid, ROPE, keys[None, None, :], block=1024)
+    check_close("dK (head 39, tail-split keys)", dk[0, keys, h], rk[0, 0])
+    check_close("dV (head 39, tail-split keys)", dv[0, keys, h], rv[0, 0])
