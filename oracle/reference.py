@@ -447,8 +447,10 @@ def self_bwd_dkdv_rows(q, k, v, dout, scale: float, grid, rope, key_rows, heads=
                 do = np.asarray(dout[b, idx, h, :], dtype=np.float64)
                 s = scale * (qt @ kt.T)
                 m = s.max(axis=1, keepdims=True)
-                lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
-                p = np.exp(s - lse[:, None])
+                # P_ij = exp(s_ij - m_i) / sum_j exp(s_ij - m_i): the softmax by its definition, with
+                # one exponential per score (the L x L scores dominate this function's time)
+                p = np.exp(np.subtract(s, m, out=s), out=s)
+                p /= p.sum(axis=1, keepdims=True)
                 delta = (do * (p @ vv)).sum(axis=1)
                 pj = p[:, J]
                 dsj = pj * (do @ vv[J].T - delta[:, None])
