@@ -126,6 +126,13 @@ def make_inputs(index: int, with_dout: bool | None = None, rows_per_head: int = 
     return out
 
 
+def workload_k_lens(index: int) -> np.ndarray:
+    """The valid text lengths of cross-attention workload `index` alone (the same draw as make_inputs)."""
+    w = WORKLOADS[index]
+    lo, hi = w.k_len_range
+    return streams(index)["k_lens"].integers(lo, hi + 1, size=w.B, dtype=np.int64).astype(np.int32)
+
+
 def random_bf16(seed: int, shape, scale: float = 1.0) -> np.ndarray:
     """Small ad-hoc bf16 tensors for edge-case tests: N(0, scale^2) rounded to bf16 bits."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))

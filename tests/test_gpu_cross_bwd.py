@@ -57,8 +57,8 @@ def test_cross_bwd_masking_edge_cases():
             assert np.abs(rq[b]).max() < 1e-12 and np.abs(rk[b, :1]).max() < 1e-12
             check_close("dQ", dq[b], rq[b], rel_l2=np.inf)
             check_close("dK", dk[b, :1], rk[b, :1], rel_l2=np.inf)
-            # dV_0 = sum of all 150 dO rows (|dV| ~ 40, not O(1)): absolute bar relative to its peak
-            check_close("dV", dv[b, :1], rv[b, :1], unit_scale=False)
+            # dV_0 = sum of all 150 dO rows (|dV| up to ~40, not O(1)): the bar adds the bf16 output quantum
+            check_close("dV", dv[b, :1], rv[b, :1], out_quantum=True)
         elif n > 0:
             check_close("dQ", dq[b], rq[b])
             check_close("dK", dk[b, :n], rk[b, :n])
@@ -87,11 +87,11 @@ def test_cross_bwd_480p_text_workload():
     rq, rk, rv = _ref(inp["q"], inp["k"], inp["v"], inp["dout"], lens)
     check_close("dQ", dq, rq)
     for b, n in enumerate(lens):
-        # a key's gradient sums over all 32,760 queries, so |dK|, |dV| are not O(1): the absolute
-        # bar is applied relative to the reference's peak (the relative-L2 bar is unchanged)
+        # a key's gradient sums over all 32,760 queries, so |dK|, |dV| reach ~6, where rounding the
+        # output to bf16 alone can cost half an ulp (1.6e-2): the bar adds that quantum per element
         print(f"  item {b}: k_len {n}, max|dK| {np.abs(rk[b, :n]).max():.2f}, max|dV| {np.abs(rv[b, :n]).max():.2f}")
-        check_close(f"dK[{b}]", dk[b, :n], rk[b, :n], unit_scale=False)
-        check_close(f"dV[{b}]", dv[b, :n], rv[b, :n], unit_scale=False)
+        check_close(f"dK[{b}]", dk[b, :n], rk[b, :n], out_quantum=True)
+        check_close(f"dV[{b}]", dv[b, :n], rv[b, :n], out_quantum=True)
         assert np.all(dk[b, n:] == 0) and np.all(dv[b, n:] == 0)
     assert w.Lq == dq.shape[1]
 
@@ -109,6 +109,6 @@ def test_cross_bwd_720p_sampled_heads():
     heads = [0, 17, 39]
     rq, rk, rv = _ref(qb[:, :, heads], kb[:, :, heads], vb[:, :, heads], dob[:, :, heads], [n])
     check_close("dQ", dq[:, :, heads], rq)
-    check_close("dK", dk[:, :n, heads], rk[:, :n], unit_scale=False)
-    check_close("dV", dv[:, :n, heads], rv[:, :n], unit_scale=False)
+    check_close("dK", dk[:, :n, heads], rk[:, :n], out_quantum=True)   # sums over 75,600 queries
+    check_close("dV", dv[:, :n, heads], rv[:, :n], out_quantum=True)
     assert np.all(dk[:, n:] == 0) and np.all(dv[:, n:] == 0)
