@@ -8,8 +8,16 @@ One step = one pass of the whole path over one batch of the Wan-14B-shaped
 Inputs are synthetic (seeded N(0,1) in bf16) and resident in HBM before timing.
 
 The reported metric is the self-attention forward's throughput: algorithmic
-4*B*H*L^2*D flop divided by the forward's mean duration, measured with HIP
-events on the stream the library launches on, inside the timed steps.
+4*B*H*L^2*D flop divided by the forward's median duration over the timed
+steps, measured with HIP events on the stream the library launches on.
+
+After the timed steps, each of the five workloads' forward calls is timed on
+its own shape (HIP events, median over repeats): the 320-token tiny case, the
+480p 1.3B forward (32,760 tokens, 12 heads), the 480p text cross-attention
+(B=2, 12 heads, 512 text tokens with the workload's seeded valid lengths), the
+720p forward (the headline) and the 262,144-token forward (40 heads); each with
+TFLOP/s against the published bf16 dense peak and against the MFMA rate a
+plain MFMA loop reaches in the same run.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -66,6 +74,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
+    try:
+        import threadpoolctl
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        return [{"library": d.get("internal_api"), "threads": d.get("num_threads")} for d in info]
+    except Exception:   # threadpoolctl missing or unable to inspect: report nothing rather than guess
+        return []
+
+
 def cpu_baseline(inp, w, rope, scale):
     """The fp64 oracle on a bounded sample: CPU_SAMPLE_ROWS seeded query rows of every head."""
     import numpy as np
@@ -84,11 +112,16 @@ def cpu_baseline(inp, w, rope, scale):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    blas = _blas_threads()
+    threads = max([b["threads"] for b in blas if b["threads"]] or [int(os.environ.get("OMP_NUM_THREADS", cores))])
+    full_flop = 4.0 * w.B * w.H * w.L * w.L * w.D
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
             "sample": f"self-attention forward (fp64 NumPy, 3D RoPE) of {rows.shape[2]} seeded query rows "
                       f"x {w.H} heads against all {w.L} keys of the 720p workload; {dt:.2f} s",
-            "seconds": dt, "flop": flop}
+            "seconds": dt, "flop": flop, "cpu_model": _cpu_model(), "affinity_cores": cores, "blas": blas,
+            "extrapolated_full_forward_s": round(dt * full_flop / flop, 1),
+            "extrapolated_note": "EXTRAPOLATED, not measured: the sample's rate applied to the whole 720p forward "
+                                 "(all 75,600 query rows x 40 heads)"}
 
 
 def _time(fn, reps=3):
@@ -103,6 +136,94 @@ def _time(fn, reps=3):
     ev[1].record()
     torch.cuda.synchronize()
     return ev[0].elapsed_time(ev[1]) / reps
+
+
+def _median_ms(fn, reps, warm=3):
+    """Median ms of `fn` over `reps` calls, each bracketed by its own HIP events on the current stream
+    (the stream the library launches on), after `warm` untimed calls."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    n = len(t)
+    return 0.5 * (t[(n - 1) // 2] + t[n // 2])
+
+
+def measure_mfma_peak(wa):
+    """TFLOP/s of the library's plain bf16 MFMA loop on every SIMD (two waves per SIMD), median of 5."""
+    import torch
+    wgs, iters = 512, 100000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    flop = wa.measure_mfma_peak(wgs, iters, sink)
+    ms = _median_ms(lambda: wa.measure_mfma_peak(wgs, iters, sink), reps=5, warm=1)
+    return {"tflops": round(flop / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3),
+            "kernel": "v_mfma_f32_32x32x16_bf16 back to back, 4 accumulators per wave, 512 workgroups x 4 waves, "
+                      "register operands with varied values"}
+
+
+def _rate(flop, ms, peak_meas):
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+            "pct_measured_mfma_peak": round(100.0 * tf / peak_meas, 2) if peak_meas else None}
+
+
+def bench_configs(wa, torch, synth, dev, rope, peak_meas, c4_ms):
+    """Each workload's forward on its own shape (median over repeats), the 720p one from the timed steps."""
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(20250)
+
+    def rand(shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    for idx, reps in ((1, 100), (2, 20), (5, 5)):
+        w = synth.WORKLOADS[idx]
+        q, k, v = (rand((w.B, w.L, w.H, w.D)) for _ in range(3))
+        table = wa.rope_table(w.grid, rope, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+        ws = torch.empty(wa.self_fwd_workspace_bytes(w.B, w.L, w.H, w.D, True), dtype=torch.uint8, device=dev)
+        ms = _median_ms(lambda: wa.self_fwd(q, k, v, grid=w.grid, table=table, rope=rope, out=o, lse=lse,
+                                            workspace=ws), reps=reps, warm=2 if idx == 5 else 3)
+        flop = 4.0 * w.B * w.H * w.L * w.L * w.D
+        out[f"C{idx}"] = dict(workload=f"{w.name}: self-attention forward, grid {'x'.join(map(str, w.grid))} "
+                                       f"(L={w.L}), B={w.B}, H={w.H}, D=128, 3D RoPE", reps=reps,
+                              **_rate(flop, ms, peak_meas))
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+    # text cross-attention: B=2, 12 heads, 32,760 video tokens over 512 text tokens, seeded valid lengths
+    w = synth.WORKLOADS[3]
+    lens = synth.workload_k_lens(3)
+    q = rand((w.B, w.Lq, w.H, w.D))
+    k, v = rand((w.B, w.Lk, w.H, w.D)), rand((w.B, w.Lk, w.H, w.D))
+    kl = torch.from_numpy(lens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
+    ms = _median_ms(lambda: wa.cross_fwd(q, k, v, kl, out=o, lse=lse), reps=100)
+    sk = float(lens.astype("int64").sum())
+    flop = 4.0 * w.H * w.D * w.Lq * sk
+    nbytes = 2.0 * (w.B * w.Lq * w.H * w.D * 2) + sk * w.H * w.D * 4 + w.B * w.H * w.Lq * 4
+    r = _rate(flop, ms, peak_meas)
+    r.update(gbs=round(nbytes / (ms * 1e-3) / 1e9, 1), pct_hbm_peak=round(100.0 * nbytes / (ms * 1e-3) / 1e9
+                                                                          / PEAK_HBM_GBS, 2),
+             algorithmic_bytes=nbytes, bound_ms=round(max(flop / (PEAK_BF16_TFLOPS * 1e12),
+                                                          nbytes / (PEAK_HBM_GBS * 1e9)) * 1e3, 4))
+    r["pct_of_bound"] = round(100.0 * r["bound_ms"] / ms, 1)
+    out["C3"] = dict(workload=f"cross: text cross-attention forward, Lq={w.Lq}, Lk={w.Lk}, B={w.B}, H={w.H}, "
+                              f"valid lengths {lens.tolist()}", reps=100, **r)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    w = synth.WORKLOADS[4]
+    out["C4"] = dict(workload=f"720p: self-attention forward, grid 21x45x80 (L={w.L}), B=1, H=40, D=128, 3D RoPE "
+                              f"(the headline; median over the timed steps)",
+                     **_rate(4.0 * w.H * w.L * w.L * w.D, c4_ms, peak_meas))
+    return {k: out[k] for k in ("C1", "C2", "C3", "C4", "C5")}
 
 
 def bench_next_rows(wa, torch, synth, dev, rope):
@@ -265,19 +386,26 @@ def main():
         bwd_ms = [e[2].elapsed_time(e[3]) for e in events]
     log(f"timed {args.steps} steps in {elapsed:.2f} s; forward ms: {[round(x, 2) for x in fwd_ms]}")
 
+    def median(x):
+        t = sorted(x)
+        return 0.5 * (t[(len(t) - 1) // 2] + t[len(t) // 2])
+
     fwd_flop = 4.0 * B * H * L * L * D
     fwd_mean = sum(fwd_ms) / len(fwd_ms)
-    fwd_tflops = fwd_flop / (fwd_mean * 1e-3) / 1e12
+    fwd_med = median(fwd_ms)
+    fwd_tflops = fwd_flop / (fwd_med * 1e-3) / 1e12
     extra = {}
     if not args.fwd_only:
         kl = ctx["k_lens"].astype(np.int64)
         cross_flop = 4.0 * H * D * L * float(kl.sum())
         cross_bytes = 2.0 * (B * L * H * D * 2) + float(kl.sum()) * H * D * 4 + B * H * L * 4
         bwd_flop = 8.0 * B * H * L * L * D
-        cross_mean = sum(cross_ms) / len(cross_ms)
-        bwd_mean = sum(bwd_ms) / len(bwd_ms)
+        cross_mean = median(cross_ms)
+        bwd_mean = median(bwd_ms)
         extra = {
-            "fwd_ms": round(fwd_mean, 3),
+            "fwd_ms": round(fwd_med, 3),
+            "fwd_ms_mean": round(fwd_mean, 3),
+            "fwd_ms_min_max": [round(min(fwd_ms), 3), round(max(fwd_ms), 3)],
             "bwd_ms": round(bwd_mean, 3),
             "bwd_tflops": round(bwd_flop / (bwd_mean * 1e-3) / 1e12, 1),
             "cross_ms": round(cross_mean, 4),
@@ -307,6 +435,8 @@ def main():
                    "rope_theta": 10000.0, "text_tokens": 512, "parallelism": "none (1 GPU)",
                    "step": "self_fwd + cross_fwd + self_bwd" if not args.fwd_only else "self_fwd"},
         "pct_bf16_peak": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "timing": "HIP events on the library's stream around each forward call; value uses the median over "
+                  "the timed steps",
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
@@ -316,6 +446,16 @@ def main():
     result.update(extra)
     if not args.fwd_only and not args.no_extras:
         result["next_rows"] = bench_next_rows(wa, torch, synth, dev, rope)
+        log("next rows done")
+    if not args.fwd_only:
+        del q, k, v, do, o, xo, dq, dk, dv, ws_f, ws_b
+        torch.cuda.empty_cache()
+        peak = measure_mfma_peak(wa)
+        result["mfma_peak_measured"] = peak
+        result["pct_measured_mfma_peak"] = round(100.0 * fwd_tflops / peak["tflops"], 2)
+        log(f"MFMA loop: {peak['tflops']} TFLOP/s")
+        result["configs"] = bench_configs(wa, torch, synth, dev, rope, peak["tflops"], fwd_med)
+        log("per-config forward timings done")
     if not args.no_cpu_baseline:
         log("running the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(inp, w, rope, scale)

@@ -33,9 +33,10 @@
  *    Each width must be even and >= 0, d_f + d_h + d_w == D, theta > 0.
  *  Rounding.  All arithmetic is fp32 (MFMA accumulates in fp32); every
  *    fp32 -> bf16 or fp16 rounding is round-to-nearest-even.  With RoPE the
- *    score product runs in fp16: each rotated query row and each 64-key tile
- *    of rotated keys is scaled by a power of two that puts its largest
- *    |element| in [2^14, 2^15) and rounded to fp16 (exact rescaling, any
+ *    score product runs in fp16: each 64-token tile of rotated queries and
+ *    each 64-token tile of rotated keys (of one batch item and head) is
+ *    scaled by a power of two that puts its largest |element| in
+ *    [2^14, 2^15) and rounded to fp16 (exact rescaling, any
  *    finite input); the forward undoes the powers of two in fp32.  Without
  *    RoPE the bf16 inputs enter the products unrounded.  P is rounded to bf16
  *    for the PV product; the softmax sums use the unrounded fp32 values.
@@ -290,6 +291,19 @@ int wanattn_cross_bwd(const void* q, const void* k, const void* v, const int32_t
                       void* dq, void* dk, void* dv,
                       int B, int Lq, int Lk, int H, int D, float scale,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not part of the attention method): a loop of back-to-back
+ * bf16 MFMAs (v_mfma_f32_32x32x16_bf16, fp32 accumulation) on every SIMD, the
+ * rate against which the attention calls' throughput can be stated next to
+ * the published dense peak.  Launches `workgroups` workgroups of 4 waves;
+ * each wave issues 4 * iters MFMAs of 32*32*16*2 flop on register operands
+ * holding varied values, then writes one float per thread to `sink` (device,
+ * workgroups * 256 floats, contents meaningless).  Algorithmic work per call:
+ * workgroups * 4 * iters * 131072 flop.  Errors: WANATTN_ERR_NULL (sink),
+ * _SHAPE (workgroups outside [1, 2^20] or iters < 1), _ALIGN, _HIP.
+ * ------------------------------------------------------------------------- */
+int wanattn_measure_mfma_peak(float* sink, int workgroups, int iters, void* stream);
 
 #ifdef __cplusplus
 }

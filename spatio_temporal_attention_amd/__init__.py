@@ -78,6 +78,7 @@ _SIGNATURES = {
     "wanattn_cross_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "wanattn_cross_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz,
                                _vp]),
+    "wanattn_measure_mfma_peak": (_i, [_vp, _i, _i, _vp]),
 }
 
 _LIB = None
@@ -421,3 +422,17 @@ def self_fwd_fp8(q, k, v, grid=None, table=None, rope=None, scale=None, out=None
                                       _stream(q.device)))
     return o, lse
 
+
+
+MFMA_PEAK_WAVES_PER_WG = 4
+MFMA_PEAK_FLOP_PER_WAVE_ITER = 4 * 2 * 32 * 32 * 16   # four 32x32x16 MFMAs per wave and iteration
+
+
+def measure_mfma_peak(workgroups: int, iters: int, sink=None):
+    """Enqueue the library's bf16 MFMA loop (a measurement aid) on the current stream and return its
+    algorithmic flop count; time it with events on that stream."""
+    torch = _torch()
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda") if sink is None else sink
+    _need(sink, torch.float32, "sink", (workgroups * 256,))
+    _check(lib().wanattn_measure_mfma_peak(_ptr(sink), int(workgroups), int(iters), _stream(sink.device)))
+    return float(workgroups) * MFMA_PEAK_WAVES_PER_WG * iters * MFMA_PEAK_FLOP_PER_WAVE_ITER

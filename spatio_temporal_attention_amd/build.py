@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libwanattn.so")
 
 SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
-           "attn_bwd_dv.hip", "merge.hip", "validate.cpp"]
+           "attn_bwd_dv.hip", "merge.hip", "mfma_peak.hip", "validate.cpp"]
 # Per-file compiler options, each chosen by timing the file's kernels under
 # the machine schedulers.  The self-attention forward's products phase needs
 # the iterative ILP scheduler to keep LDS reads ahead of its MFMAs (the

@@ -313,3 +313,10 @@ WANATTN_API int wanattn_cross_fwd(const void* q, const void* k, const void* v, c
   p.scale_log2 = scale * LOG2E_F;
   return hip_status(launch_attn_fwd(p, (hipStream_t)stream));
 }
+
+WANATTN_API int wanattn_measure_mfma_peak(float* sink, int workgroups, int iters, void* stream) {
+  if (sink == nullptr) return WANATTN_ERR_NULL;
+  if (workgroups <= 0 || workgroups > (1 << 20) || iters <= 0) return WANATTN_ERR_SHAPE;
+  if (!aligned(sink, 4)) return WANATTN_ERR_ALIGN;
+  return hip_status(launch_mfma_peak(sink, workgroups, iters, (hipStream_t)stream));
+}

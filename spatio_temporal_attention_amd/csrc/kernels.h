@@ -107,5 +107,7 @@ hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uin
 hipError_t launch_bwd_dv(const BwdParams& p, int n_main, int n_tail, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
+// Measurement aid (mfma_peak.hip): workgroups x 4 waves, each iters x 4 back-to-back bf16 MFMAs.
+hipError_t launch_mfma_peak(float* sink, int workgroups, int iters, hipStream_t stream);
 
 }  // namespace wanattn

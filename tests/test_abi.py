@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libwanattn.so"
         assert n in wa._SIGNATURES, f"{n} has no binding"
@@ -293,3 +293,13 @@ def test_fp8_validation(lib):
     assert f8(D=64) == UNSUP
     assert f8(scale=float("inf")) == UNSUP
 
+
+
+def test_mfma_peak_argument_checks(lib):
+    """The measurement aid validates on the host (no GPU is touched on these paths)."""
+    assert lib.wanattn_measure_mfma_peak(None, 512, 10, None) == 1          # NULL sink
+    fake = ctypes.c_void_p(0x1000)                                          # never dereferenced: rejected first
+    assert lib.wanattn_measure_mfma_peak(fake, 0, 10, None) == 2
+    assert lib.wanattn_measure_mfma_peak(fake, 512, 0, None) == 2
+    assert lib.wanattn_measure_mfma_peak(fake, (1 << 20) + 1, 10, None) == 2
+    assert lib.wanattn_measure_mfma_peak(ctypes.c_void_p(0x1002), 512, 10, None) == 4   # misaligned
