@@ -13,7 +13,13 @@ them are the plain definitions of `oracle.reference`, evaluated at these rounded
 
 This module supplies the rounding and the attention at rounded operands, so that a test can separate
 what the documented operand rounding moves (the distance between `self_fwd_fp16_ref` and the exact
-`self_fwd_ref`) from any other difference. Rounding is numpy's float64 -> float16 conversion (a library
+`self_fwd_ref`) from any other difference.
+
+The rounding of a value is unique except next to a rounding tie: the library rotates in fp32, whose
+result may lie on the other side of a tie than the exact rotation this module rounds, and then rounds
+to the neighbouring fp16 value (about one element in 10^4 for random inputs). `ambiguous_elements`
+marks every element where that can happen, from the exact values alone, and `score_tie_allowance`
+bounds how far such alternative roundings can move a row's LSE and output. Rounding is numpy's float64 -> float16 conversion (a library
 primitive); tests/test_oracle_fp16.py pins it against binary16 code points built from the format's
 definition and pins the tile recipe, the attention at rounded operands and the rounding bound.
 """
@@ -71,10 +77,11 @@ def self_fwd_fp16_ref(q, k, v, scale: float, grid, rope, rows=None):
     return self_fwd_ref(qt, kt, v, scale, rows=rows)
 
 
-def self_bwd_fp16_ref(q, k, v, dout, scale: float, grid, rope):
+def self_bwd_fp16_ref(q, k, v, dout, scale: float, grid, rope, o=None):
     """dQ, dK, dV (w.r.t. the unrotated q and k) of attention evaluated at the fp16-rounded rotated
     operands: the plain backward of `oracle.reference` with q~, k~ replaced by their rounded tiles,
-    the gradients rotated back by minus the angle."""
+    the gradients rotated back by minus the angle.  o (optional, [B, L, H, D]): the forward output
+    handed to the backward, from which Delta_i = <dO_i, o_i> is formed (default: this function's own)."""
     qt, kt = rounded_operands(q, k, grid, rope)
     B, L, H, D = q.shape
     idx = np.arange(L)
@@ -84,11 +91,75 @@ def self_bwd_fp16_ref(q, k, v, dout, scale: float, grid, rope):
     for b in range(B):
         for h in range(H):
             dqt, dkt, dvh = _head_bwd(qt[b, :, h, :], kt[b, :, h, :], np.asarray(v[b, :, h, :], dtype=np.float64),
-                                      np.asarray(dout[b, :, h, :], dtype=np.float64), scale)
+                                      np.asarray(dout[b, :, h, :], dtype=np.float64), scale,
+                                      None if o is None else o[b, :, h, :])
             dq[b, :, h, :] = _rotated(dqt, idx, grid, rope, inverse=True)
             dk[b, :, h, :] = _rotated(dkt, idx, grid, rope, inverse=True)
             dv[b, :, h, :] = dvh
     return dq, dk, dv
+
+
+FP32_ROTATION_ERR = 2.0 ** -22   # |fp32 rotation - exact| <= this * (|x_2j| + |x_2j+1|) of the input pair
+
+
+def _pair_magnitude(x):
+    """|x_2j| + |x_2j+1| for each element's rotation pair, [B, L, H, D]."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    s = a[..., 0::2] + a[..., 1::2]
+    return np.repeat(s, 2, axis=-1)
+
+
+def ambiguous_elements(x, grid, rope, tile: int = TILE):
+    """(mask, ulp) for x [B, L, H, D] (unrotated): mask marks the elements whose fp16 tile rounding may
+    differ from this module's when the rotation is computed in fp32 (the exact rotated value lies within
+    the fp32 rotation's error bound of a rounding tie, or the tile's exponent itself is in doubt, in which
+    case the whole tile is marked); ulp is the fp16 spacing at each rounded element, in unscaled units."""
+    xr = _rot(x, grid, rope)
+    err = FP32_ROTATION_ERR * _pair_magnitude(x) if rope is not None else np.zeros_like(xr)
+    B, L, H, D = xr.shape
+    mask = np.zeros(xr.shape, bool)
+    ulp = np.zeros(xr.shape)
+    for b in range(B):
+        for h in range(H):
+            for t0 in range(0, L, tile):
+                blk = xr[b, t0:t0 + tile, h, :]
+                eb = err[b, t0:t0 + tile, h, :]
+                mx = float(np.abs(blk).max())
+                e = tile_exponent15(mx)
+                z = np.abs(blk) * 2.0 ** -e
+                u = np.exp2(np.floor(np.log2(np.maximum(z, 2.0 ** -14))) - 10)   # fp16 spacing at z
+                frac = z / u - np.floor(z / u)
+                near = np.abs(frac - 0.5) * u <= eb * 2.0 ** -e
+                me = float(eb.max())
+                if tile_exponent15(mx + me) != e or tile_exponent15(max(mx - me, 0.0)) != e:
+                    near[:] = True
+                mask[b, t0:t0 + tile, h, :] = near
+                ulp[b, t0:t0 + tile, h, :] = u * 2.0 ** e
+    return mask, ulp
+
+
+def score_tie_allowance(q, k, scale: float, grid, rope) -> np.ndarray:
+    """Per query row ([B, H, L]) a bound A_i on how far alternative roundings of ambiguous elements can
+    move the row's LSE.  Each ambiguous element may land one fp16 ulp away, so score s_ij moves by at most
+    D_ij = scale * (sum_{d amb in q_i} ulp_id |k~_jd| + sum_{d amb in k_j} |q~_id| ulp_jd).  Since
+    LSE(s + delta) - LSE(s) = ln sum_j P_ij exp(delta_ij), |dLSE_i| <= A_i = ln sum_j P_ij exp(D_ij) (P at
+    the rounded operands), and the softmax weights move by at most sum_j |dP_ij| <= exp(2 A_i) - 1, so
+    |dO_i| <= (exp(2 A_i) - 1) max_j |v_j| elementwise."""
+    qm, qu = ambiguous_elements(q, grid, rope)
+    km, ku = ambiguous_elements(k, grid, rope)
+    qr, kr = rounded_operands(q, k, grid, rope)
+    B, L, H, D = qr.shape
+    out = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            qh, kh = qr[b, :, h, :], kr[b, :, h, :]
+            dmax = float(scale) * ((qm[b, :, h, :] * qu[b, :, h, :]) @ np.abs(kh).T
+                                   + np.abs(qh) @ (km[b, :, h, :] * ku[b, :, h, :]).T)     # [L, Lk]
+            s = float(scale) * (qh @ kh.T)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            out[b, h] = np.log((p * np.exp(dmax)).sum(axis=1))
+    return out
 
 
 def score_rounding_bound(q, k, scale: float, grid, rope) -> np.ndarray:

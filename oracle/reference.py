@@ -336,15 +336,18 @@ def lse_merge_ref(o_parts, lse_parts):
     return o, tot
 
 
-def _head_bwd(qt, kt, v, dout, scale):
-    """Gradients of sum(dout * O) w.r.t. the rotated qt, kt and v of one head (full L x N)."""
+def _head_bwd(qt, kt, v, dout, scale, o_given=None):
+    """Gradients of sum(dout * O) w.r.t. the rotated qt, kt and v of one head (full L x N).
+
+    o_given: the forward output the caller hands to the backward (as the library's backward takes
+    o); Delta is then formed from it instead of from this function's own O."""
     if kt.shape[0] == 0:
         return np.zeros_like(qt), np.zeros_like(kt), np.zeros_like(v)
     s = scale * (qt @ kt.T)
     m = s.max(axis=1, keepdims=True)
     lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
     p = np.exp(s - lse[:, None])
-    o = p @ v
+    o = p @ v if o_given is None else np.asarray(o_given, dtype=np.float64)
     delta = (dout * o).sum(axis=1)                      # Delta_i = <dO_i, O_i>
     dv = p.T @ dout                                     # dV_j = sum_i P_ij dO_i
     dp = dout @ v.T                                     # dP_ij = <dO_i, v_j>

@@ -171,3 +171,78 @@ def test_fp16_backward_is_the_gradient_at_rounded_operands():
         num_k = (f(qt[0, :, 0], kt[0, :, 0] + e) - f(qt[0, :, 0], kt[0, :, 0] - e)) / (2 * h)
         assert abs(num_q - dqt[i, d]) < 1e-6 * max(1.0, abs(num_q))
         assert abs(num_k - dkt[i, d]) < 1e-6 * max(1.0, abs(num_k))
+
+
+def _fp32_rotation(x, grid):
+    """A rotation computed in fp32 (fp32 table, one fused multiply-add per output), rounded per step as an
+    fp32 machine would: a test-side stand-in for any fp32 implementation of the rotation."""
+    pos = oracle.positions(grid)
+    ang = oracle.rope_angles(pos, ROPE, 128)
+    c = np.cos(ang).astype(np.float32).astype(np.float64)[:, None, :]
+    s = np.sin(ang).astype(np.float32).astype(np.float64)[:, None, :]
+    x0, x1 = x[0, :, :, 0::2], x[0, :, :, 1::2]
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)
+    y = np.empty_like(x)
+    y[0, :, :, 0::2] = f32(x0 * c - f32(x1 * s))
+    y[0, :, :, 1::2] = f32(x0 * s + f32(x1 * c))
+    return y
+
+
+def test_ambiguous_elements_cover_fp32_rotation_flips():
+    """Every element whose fp16 tile rounding differs between an fp32 and the exact rotation is marked
+    ambiguous, and the marked set is small (the allowance stays tight)."""
+    grid = (5, 8, 8)
+    flips = marked = total = 0
+    for seed, qmul in ((5328, 8.0), (5324, 4.0), (77, 1.0)):
+        q = synth.bf16_bits_to_f64(synth.random_bf16(seed, (1, 320, 2, 128), scale=qmul))
+        r32 = f16.round_tiles(_fp32_rotation(q, grid))
+        r64 = f16.round_tiles(oracle.rope3d_ref(q, grid, ROPE))
+        mask, ulp = f16.ambiguous_elements(q, grid, ROPE)
+        diff = r32 != r64
+        assert np.all(mask[diff]), "an fp32-rotation rounding flip was not marked ambiguous"
+        assert np.all(np.abs(r32 - r64)[diff] <= ulp[diff] * (1 + 1e-12))   # one ulp apart
+        flips += int(diff.sum())
+        marked += int(mask.sum())
+        total += mask.size
+    assert flips > 0                      # the inputs do produce flips (the check has teeth)
+    assert marked < 1e-2 * total, (marked, total)
+    print(f"  flips {flips}, marked {marked} of {total}")
+
+
+def test_tie_allowance_covers_fp32_rotation_flips():
+    """Attention at the fp16 roundings of an fp32 rotation stays within the tie allowance of the module's
+    own rounding, row by row, for peaked inputs."""
+    grid = (5, 8, 8)
+    q, k, v, _ = _peaked(5328, grid, 8.0)
+    _, l_ref = f16.self_fwd_fp16_ref(q, k, v, SCALE, grid, ROPE)
+    _, l_32 = oracle.self_fwd_ref(f16.round_tiles(_fp32_rotation(q, grid)),
+                                  f16.round_tiles(_fp32_rotation(k, grid)), v, SCALE)
+    allow = f16.score_tie_allowance(q, k, SCALE, grid, ROPE)
+    d = np.abs(l_32 - l_ref)
+    assert np.all(d <= allow + 1e-12)
+    assert d.max() > 1e-4                 # flips do move some rows
+    print(f"  max |dLSE| {d.max():.2e}; allowance there {allow.flat[np.argmax(d)]:.2e}, max {allow.max():.2e}")
+
+
+def test_backward_with_a_given_output():
+    """Delta from a handed-in output: with the function's own output it is the default; with another
+    output only Delta (hence dS, dQ, dK) moves, dV not at all, by exactly the change of Delta."""
+    grid = (2, 3, 4)
+    q, k, v, do = _peaked(95, grid, 4.0, H=1)
+    qt, kt = f16.rounded_operands(q, k, grid, ROPE)
+    o, _ = oracle.self_fwd_ref(qt, kt, v, SCALE)
+    for a, b in zip(f16.self_bwd_fp16_ref(q, k, v, do, SCALE, grid, ROPE, o=o),
+                    f16.self_bwd_fp16_ref(q, k, v, do, SCALE, grid, ROPE)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    o2 = o + 0.01 * synth.bf16_bits_to_f64(synth.random_bf16(96, o.shape))
+    dq1, dk1, dv1 = f16.self_bwd_fp16_ref(q, k, v, do, SCALE, grid, ROPE)
+    dq2, dk2, dv2 = f16.self_bwd_fp16_ref(q, k, v, do, SCALE, grid, ROPE, o=o2)
+    np.testing.assert_array_equal(dv1, dv2)
+    # dq~_i changes by -scale * dDelta_i * sum_j P_ij k~_j
+    s = SCALE * (qt[0, :, 0] @ kt[0, :, 0].T)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    d_delta = (do[0, :, 0] * (o2 - o)[0, :, 0]).sum(axis=1)
+    pos = oracle.positions(grid)
+    ddq_rot = oracle.rope_apply((dq2 - dq1)[0, :, 0], oracle.rope_angles(pos, ROPE, 128))
+    np.testing.assert_allclose(ddq_rot, -SCALE * d_delta[:, None] * (p @ kt[0, :, 0]), rtol=1e-9, atol=1e-12)
