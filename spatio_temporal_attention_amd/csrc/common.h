@@ -150,24 +150,15 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
 }
 
-// Direct global -> LDS staging of a 64-row tile by 4 waves (no registers):
-// wave w fills rows 16w .. 16w+15 with four 1 KB global_load_lds_dwordx4
-// instructions; lane l of an instruction lands at LDS byte 16*l of its 1 KB
-// block, i.e. row 16w + 4i + l/16, physical chunk l%16, so it fetches the
-// logical chunk (l%16) ^ swz(row).  Rows at or past `nrows` fetch row
-// nrows-1 instead (always valid data; callers mask those rows out), so no
-// padded or out-of-range memory is read.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void tile_dma(uint16_t* lds_tile, const uint16_t* base, int64_t row_stride, int row0,
-                                         int nrows, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rblk = 16 * wave + 4 * i;
-    const int r = rblk + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
-    const int grow = min(row0 + r, nrows - 1);
-    const uint16_t* src = base + (int64_t)grow * row_stride + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_tile + rblk * HD), 16, 0, 0);
-  }
+// Lane byte offset of the global -> LDS staging of 64 rows of a row-major
+// [.., L, H, 128] bf16 tensor (row r at byte r * row_bytes) by 4 waves: copy
+// i of wave w (1 KB, LDS block tile_lds_block<4>(tile, w, i)) covers tile
+// rows 16w + 4i + l/16; lane l fetches logical chunk (l%16) ^ swz(row) into
+// physical chunk l%16, the layout of tile_off.  The tile's first row goes in
+// the copy's scalar offset, so these offsets hold for every tile.
+__device__ __forceinline__ uint32_t rows_lane_off(int wave, int i, int lane, uint32_t row_bytes) {
+  const int r = 16 * wave + 4 * i + (lane >> 4);
+  return (uint32_t)r * row_bytes + ((uint32_t)((lane & 15) ^ swz(r)) << 4);
 }
 
 // Read-only arrays (not written during the kernel) read through the
