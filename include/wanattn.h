@@ -293,6 +293,28 @@ int wanattn_cross_bwd(const void* q, const void* k, const void* v, const int32_t
                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Allocation-free variant of wanattn_self_fwd, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, semantics and results as
+ * wanattn_self_fwd (the same kernels run), minus the workspace: the K/V tiles
+ * and the tail split's partials go to a static device array of the library,
+ * 256 MiB per GPU, held from the library's load until the process ends.  The
+ * call allocates and frees nothing.  Its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress) with the device current.
+ * Limit: wanattn_self_fwd_workspace_bytes(B, L, H, D, table != NULL) must not
+ * exceed 268435456 (for example B*H*L up to about 500,000 token-heads with
+ * RoPE: L = 32,760 with 12 heads, or 75,600 with 5); larger problems return
+ * WANATTN_ERR_WORKSPACE before anything is enqueued.  All calls on one GPU
+ * share its array: calls that overlap on that GPU (different streams or host
+ * threads without ordering between them) race and give undefined results;
+ * calls ordered on one stream are safe.  Nothing in the array needs to start
+ * at zero (every byte read is written earlier in the same call).
+ * ------------------------------------------------------------------------- */
+int wanattn_self_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
+                             const float* table, float scale, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement aid (not part of the attention method): a loop of back-to-back
  * bf16 MFMAs (v_mfma_f32_32x32x16_bf16, fp32 accumulation) on every SIMD, the
  * rate against which the attention calls' throughput can be stated next to

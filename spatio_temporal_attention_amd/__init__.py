@@ -79,6 +79,7 @@ _SIGNATURES = {
     "wanattn_cross_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz,
                                _vp]),
     "wanattn_measure_mfma_peak": (_i, [_vp, _i, _i, _vp]),
+    "wanattn_self_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, Grid, Rope, _vp, _f, _vp]),
 }
 
 _LIB = None
@@ -227,6 +228,26 @@ def self_fwd(q, k, v, grid=None, table=None, rope=None, scale=None, out=None, ls
                                   _ptr(table), scale, _ptr(ws), nbytes if ws is None else ws.numel(),
                                   _stream(q.device)))
     return o, lse
+
+
+def self_fwd_noalloc(q, k, v, out, lse=None, grid=None, table=None, rope=None, scale=None):
+    """wanattn_self_fwd without a workspace (the library's static scratch instead): the caller passes the
+    output `out` and optionally `lse`; nothing is allocated here or in the call.  Returns (out, lse)."""
+    torch = _torch()
+    _need(q, torch.bfloat16, "q")
+    B, L, H, D = q.shape
+    _need(k, torch.bfloat16, "k", q.shape)
+    _need(v, torch.bfloat16, "v", q.shape)
+    _need(out, torch.bfloat16, "out", q.shape)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (B, H, L))
+    if table is not None:
+        _need(table, torch.float32, "table")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    g = _grid(grid if grid is not None else (1, 1, L))
+    _check(lib().wanattn_self_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, L, H, D, g,
+                                          _rope(rope), _ptr(table), scale, _stream(q.device)))
+    return out, lse
 
 
 def self_bwd(q, k, v, o, lse, dout, grid=None, table=None, rope=None, scale=None, workspace=None,

@@ -2,6 +2,8 @@
 // argument validation on the host, then launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/wanattn.h"
 #include "kernels.h"
 #include "validate.h"
@@ -47,7 +49,9 @@ WANATTN_API const char* wanattn_strerror(int status) {
       return "wanattn: unsupported argument (head dim must be 128; rotary split must be even widths summing to "
              "128; theta > 0; finite scale)";
     case WANATTN_ERR_ALIGN: return "wanattn: misaligned buffer (bf16/table/workspace need 16 bytes, fp32/int32 4)";
-    case WANATTN_ERR_WORKSPACE: return "wanattn: workspace missing or too small";
+    case WANATTN_ERR_WORKSPACE:
+      return "wanattn: workspace missing or too small (wanattn_self_fwd_noalloc: the problem needs more than its "
+             "256 MiB static scratch)";
     case WANATTN_ERR_HIP: return "wanattn: HIP launch failed";
     default: return "wanattn: unknown status";
   }
@@ -132,6 +136,58 @@ WANATTN_API int wanattn_self_fwd(const void* q, const void* k, const void* v, vo
                                  void* ws, size_t ws_bytes, void* stream) {
   const int rc = validate_self_fwd(q, k, v, o, lse, B, L, H, D, g, r, table, scale, ws, ws_bytes);
   if (rc != WANATTN_OK) return rc;
+  return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, nullptr, 0, 0, true, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free self-attention forward.  For callers that cannot allocate
+// device memory (code under HIP graph capture, tight serving loops, harnesses
+// that forbid hipMalloc): the forward's workspace (the K/V tiles and the tail
+// split's partials) lives in one static device array per GPU instead of a
+// caller buffer.
+// ---------------------------------------------------------------------------
+namespace wanattn {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)256 << 20;   // 256 MiB per GPU, held until the process ends
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES];   // device address of each GPU's copy of `scratch`, looked up once
+
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address of the current GPU's copy comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// ever passed to a kernel.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return WANATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return WANATTN_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return WANATTN_OK;
+}
+
+}  // namespace
+}  // namespace wanattn
+
+WANATTN_API int wanattn_self_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                         int L, int H, int D, wanattn_grid g, wanattn_rope r, const float* table,
+                                         float scale, void* stream) {
+  const int rc = validate_self_fwd_args(q, k, v, o, lse, B, L, H, D, g, r, table, scale);
+  if (rc != WANATTN_OK) return rc;
+  if (self_fwd_ws_bytes(B, L, H, D, table != nullptr) > NOALLOC_SCRATCH_BYTES) return WANATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int e = scratch_address(&ws);
+  if (e != WANATTN_OK) return e;
+  // The same launches as wanattn_self_fwd; every byte of the scratch they read
+  // is written earlier in the same call, so nothing needs clearing.
   return run_self_fwd(q, k, v, o, lse, B, L, L, H, D, g, r, table, scale, ws, nullptr, 0, 0, true, (hipStream_t)stream);
 }
 

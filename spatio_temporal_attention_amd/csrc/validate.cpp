@@ -190,9 +190,8 @@ int validate_rope3d(const void* x, const void* y, int B, int L, int H, int D, wa
   return WANATTN_OK;
 }
 
-int validate_self_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int L,
-                      int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
-                      const void* ws, size_t ws_bytes) {
+int validate_self_fwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                           int L, int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return WANATTN_ERR_NULL;
   WANATTN_TRY(check_dims(B, L, H, D));
   if (table != nullptr) WANATTN_TRY(check_grid_rope(g, r, L, D));
@@ -203,6 +202,13 @@ int validate_self_fwd(const void* q, const void* k, const void* v, const void* o
   WANATTN_TRY(check_bf16(o));
   if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
   if (table != nullptr && !aligned(table, 16)) return WANATTN_ERR_ALIGN;
+  return WANATTN_OK;
+}
+
+int validate_self_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int L,
+                      int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
+                      const void* ws, size_t ws_bytes) {
+  WANATTN_TRY(validate_self_fwd_args(q, k, v, o, lse, B, L, H, D, g, r, table, scale));
   if (ws == nullptr || ws_bytes < self_fwd_ws_bytes(B, L, H, D, table != nullptr)) return WANATTN_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
   return WANATTN_OK;

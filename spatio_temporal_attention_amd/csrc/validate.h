@@ -78,6 +78,9 @@ size_t cross_bwd_ws_bytes(int B, int Lq, int Lk, int H, int D);
 
 int validate_rope3d(const void* x, const void* y, int B, int L, int H, int D, wanattn_grid g, wanattn_rope r,
                     const float* table);
+// Every check of validate_self_fwd except the workspace's.
+int validate_self_fwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                           int L, int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale);
 int validate_self_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int L,
                       int H, int D, wanattn_grid g, wanattn_rope r, const float* table, float scale,
                       const void* ws, size_t ws_bytes);
