@@ -205,7 +205,8 @@ def bench_configs(wa, torch, synth, dev, rope, peak_meas, c4_ms):
     kl = torch.from_numpy(lens).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
-    ms = _median_ms(lambda: wa.cross_fwd(q, k, v, kl, out=o, lse=lse), reps=100)
+    xws = torch.empty(wa.cross_fwd_workspace_bytes(w.B, w.Lk, w.H, w.D), dtype=torch.uint8, device=dev)
+    ms = _median_ms(lambda: wa.cross_fwd(q, k, v, kl, out=o, lse=lse, workspace=xws), reps=100)
     sk = float(lens.astype("int64").sum())
     flop = 4.0 * w.H * w.D * w.Lq * sk
     nbytes = 2.0 * (w.B * w.Lq * w.H * w.D * 2) + sk * w.H * w.D * 4 + w.B * w.H * w.Lq * 4
@@ -350,6 +351,7 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws_f = torch.empty(wa.self_fwd_workspace_bytes(B, L, H, D, True), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(wa.self_bwd_workspace_bytes(B, L, H, D, True), dtype=torch.uint8, device=dev)
+    ws_x = torch.empty(wa.cross_fwd_workspace_bytes(B, tk.shape[1], H, D), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -360,7 +362,7 @@ def main():
             ev[1].record()
         if args.fwd_only:
             return
-        wa.cross_fwd(q, tk, tv, k_lens, scale=scale, out=xo, lse=xlse)
+        wa.cross_fwd(q, tk, tv, k_lens, scale=scale, out=xo, lse=xlse, workspace=ws_x)
         if ev is not None:
             ev[2].record()
         wa.self_bwd(q, k, v, o, lse, do, grid=w.grid, table=table, rope=rope, scale=scale, workspace=ws_b,
@@ -448,7 +450,7 @@ def main():
         result["next_rows"] = bench_next_rows(wa, torch, synth, dev, rope)
         log("next rows done")
     if not args.fwd_only:
-        del q, k, v, do, o, xo, dq, dk, dv, ws_f, ws_b
+        del q, k, v, do, o, xo, dq, dk, dv, ws_f, ws_b, ws_x
         torch.cuda.empty_cache()
         peak = measure_mfma_peak(wa)
         result["mfma_peak_measured"] = peak

@@ -259,10 +259,18 @@ int wanattn_lse_merge(const void* const* o_parts, const float* const* lse_parts,
  * NaN included).  k_lens: device int32 [B], each clamped to [0, Lk]; NULL
  * means every key is valid.  A row with no valid key gets O = 0 and
  * LSE = -inf.  lse may be NULL.
+ * Workspace (required, 16-byte aligned): wanattn_cross_fwd_workspace_bytes(B,
+ * Lk, H, D) bytes.  It receives the text keys and values rewritten in 64-key
+ * tiles of every (b, h): K as [B, H, ceil(Lk/64), 64, D] bf16 and V
+ * transposed as [B, H, ceil(Lk/64), D, 64] bf16, keys past k_lens[b] zero;
+ * each part starts on a 256-byte boundary (10.5 MB at Lk = 512, H = 40).  Its
+ * contents on return are unspecified.
  * ------------------------------------------------------------------------- */
+size_t wanattn_cross_fwd_workspace_bytes(int B, int Lk, int H, int D);
+
 int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens,
-                      void* o, float* lse,
-                      int B, int Lq, int Lk, int H, int D, float scale, void* stream);
+                      void* o, float* lse, int B, int Lq, int Lk, int H, int D, float scale,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Cross-attention backward (training back-propagates through the text

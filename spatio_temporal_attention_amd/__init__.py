@@ -66,7 +66,8 @@ _SIGNATURES = {
     "wanattn_self_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "wanattn_self_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, Grid, Rope, _vp, _f,
                               _vp, _sz, _vp]),
-    "wanattn_cross_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "wanattn_cross_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "wanattn_cross_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "wanattn_self_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, Grid, Rope, _vp, _f, _vp, _sz,
                                      _vp]),
     "wanattn_partial_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
@@ -276,7 +277,11 @@ def self_bwd(q, k, v, o, lse, dout, grid=None, table=None, rope=None, scale=None
     return dq, dk, dv
 
 
-def cross_fwd(q, k, v, k_lens=None, scale=None, out=None, lse=None, want_lse=True):
+def cross_fwd_workspace_bytes(B, Lk, H, D=HEAD_DIM) -> int:
+    return int(lib().wanattn_cross_fwd_workspace_bytes(B, Lk, H, D))
+
+
+def cross_fwd(q, k, v, k_lens=None, scale=None, out=None, lse=None, want_lse=True, workspace=None):
     """Cross-attention forward over key-padded text tokens.  Returns (o, lse)."""
     torch = _torch()
     _need(q, torch.bfloat16, "q")
@@ -294,8 +299,10 @@ def cross_fwd(q, k, v, k_lens=None, scale=None, out=None, lse=None, want_lse=Tru
     if lse is not None:
         _need(lse, torch.float32, "lse", (B, H, Lq))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = cross_fwd_workspace_bytes(B, Lk, H, D)
+    ws = _workspace(nbytes, q.device, workspace)
     _check(lib().wanattn_cross_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(k_lens), _ptr(o), _ptr(lse), B, Lq, Lk, H, D,
-                                   scale, _stream(q.device)))
+                                   scale, _ptr(ws), nbytes if ws is None else ws.numel(), _stream(q.device)))
     return o, lse
 
 

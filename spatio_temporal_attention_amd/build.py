@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libwanattn.so")
 
-SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
+SOURCES = ["api.hip", "rope.hip", "kv_prep.hip", "attn_fwd_pp.hip", "attn_fwd_fp8.hip", "attn_bwd.hip",
            "attn_bwd_dv.hip", "merge.hip", "mfma_peak.hip", "validate.cpp"]
 # Per-file compiler options, each chosen by timing the file's kernels under
 # the machine schedulers.  The self-attention forward's products phase needs

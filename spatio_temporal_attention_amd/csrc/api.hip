@@ -125,7 +125,7 @@ int run_self_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
   p.part = (tail_split && wl.part != 0) ? (float*)((uint8_t*)ws + wl.part) : nullptr;
-  return hip_status(launch_attn_fwd(p, s));
+  return hip_status(launch_attn_fwd_tiled(p, s));
 }
 
 }  // namespace
@@ -350,10 +350,25 @@ WANATTN_API int wanattn_cross_bwd(const void* q, const void* k, const void* v, c
                  scale, ws, (hipStream_t)stream);
 }
 
+WANATTN_API size_t wanattn_cross_fwd_workspace_bytes(int B, int Lk, int H, int D) {
+  return fwd_tiles_ws_bytes(B, Lk, H, D, 0);
+}
+
 WANATTN_API int wanattn_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, void* o,
-                                  float* lse, int B, int Lq, int Lk, int H, int D, float scale, void* stream) {
-  const int rc = validate_cross_fwd(q, k, v, k_lens, o, lse, B, Lq, Lk, H, D, scale);
+                                  float* lse, int B, int Lq, int Lk, int H, int D, float scale, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  const int rc = validate_cross_fwd(q, k, v, k_lens, o, lse, B, Lq, Lk, H, D, scale, ws, ws_bytes);
   if (rc != WANATTN_OK) return rc;
+  // The text keys and values rewritten once into the forward's 64-key tiles
+  // (bf16 K, transposed V; keys past k_lens[b] zero and never read), then the
+  // self-attention kernel over them with Lq != Lk, the key mask and no RoPE.
+  const RopeDev rope = make_rope(wanattn_grid{1, 1, 1}, wanattn_rope{0, 0, 0, 1.f}, nullptr);
+  const FwdWsLayout wl = self_fwd_ws_layout(B, Lk, H, D, 0);
+  uint16_t* kt = (uint16_t*)((uint8_t*)ws + wl.kt);
+  uint16_t* vt = (uint16_t*)((uint8_t*)ws + wl.vt);
+  const int e = hip_status(launch_kv_tiles((const uint16_t*)k, (const uint16_t*)v, kt, nullptr, vt, B, Lk, H, rope,
+                                           k_lens, 0, (hipStream_t)stream));
+  if (e != WANATTN_OK) return e;
   FwdParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -361,13 +376,15 @@ WANATTN_API int wanattn_cross_fwd(const void* q, const void* k, const void* v, c
   p.o = (uint16_t*)o;
   p.lse = lse;
   p.k_lens = k_lens;
-  p.rope = make_rope(wanattn_grid{1, 1, 1}, wanattn_rope{0, 0, 0, 1.f}, nullptr);
+  p.kt = kt;
+  p.vt = vt;
+  p.rope = rope;
   p.B = B;
   p.Lq = Lq;
   p.Lk = Lk;
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
-  return hip_status(launch_attn_fwd(p, (hipStream_t)stream));
+  return hip_status(launch_attn_fwd_tiled(p, (hipStream_t)stream));
 }
 
 WANATTN_API int wanattn_measure_mfma_peak(float* sink, int workgroups, int iters, void* stream) {

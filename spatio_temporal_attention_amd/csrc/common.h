@@ -2,10 +2,11 @@
 //
 // * bf16 <-> fp32 helpers (fp32 -> bf16 is round-to-nearest-even via v_cvt_pk_bf16_f32)
 // * the 3D RoPE rotation of one (even, odd) element pair
-// * staging of 64-row x 128-column bf16 tiles into LDS in a row-major layout
-//   whose 16-byte chunks are XOR-swizzled per row, read back either as
-//   16-byte row fragments (MFMA operands whose k index runs along the row) or
-//   through the LDS transpose read (operands whose k index runs down a column)
+// * staging of 64-row x 128-column tiles into LDS in a row-major layout whose
+//   16-byte chunks are XOR-swizzled per row, read back as 16-byte row
+//   fragments (MFMA operands whose k index runs along the row), and of
+//   transposed (T) tiles whose rows feed the products that contract over
+//   tokens
 // * MFMA 32x32x16 bf16 wrappers and their register layouts.
 #pragma once
 
@@ -25,11 +26,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ---------------------------------------------------------------------------
 // bf16 helpers
@@ -135,11 +134,8 @@ __device__ __forceinline__ u32x4 rope_chunk(const RopeDev& r, const TokenPos& p,
 // The 16 chunks (16 bytes each) of row r are stored at chunk c ^ swz(r).
 // LDS has 64 banks of 4 bytes, so a row spans all banks once and a chunk's
 // bank group is its physical index.  swz(r) = ((r&3) << 2) | ((r>>2)&3):
-//  (a) 16 consecutive rows read at one logical chunk (16-byte row fragments,
-//      16 lanes per LDS cycle) land on 16 distinct chunks;
-//  (b) a 32-lane pass of the transpose read covers 4 rows 4m+e (e = 0..3) x
-//      4 aligned logical chunks; bits 2-3 of swz differ across e, so the rows
-//      land on 4 disjoint aligned chunk groups.
+// 16 consecutive rows read at one logical chunk (16-byte row fragments, 16
+// lanes per LDS cycle) land on 16 distinct chunks.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz(int r) {
   return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -148,17 +144,6 @@ __device__ __forceinline__ int swz(int r) {
 // Offset (in bf16 elements) of element (row, col) inside a tile; col % 8 kept.
 __device__ __forceinline__ int tile_off(int row, int col) {
   return row * HD + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
-}
-
-// Lane byte offset of the global -> LDS staging of 64 rows of a row-major
-// [.., L, H, 128] bf16 tensor (row r at byte r * row_bytes) by 4 waves: copy
-// i of wave w (1 KB, LDS block tile_lds_block<4>(tile, w, i)) covers tile
-// rows 16w + 4i + l/16; lane l fetches logical chunk (l%16) ^ swz(row) into
-// physical chunk l%16, the layout of tile_off.  The tile's first row goes in
-// the copy's scalar offset, so these offsets hold for every tile.
-__device__ __forceinline__ uint32_t rows_lane_off(int wave, int i, int lane, uint32_t row_bytes) {
-  const int r = 16 * wave + 4 * i + (lane >> 4);
-  return (uint32_t)r * row_bytes + ((uint32_t)((lane & 15) ^ swz(r)) << 4);
 }
 
 // Read-only arrays (not written during the kernel) read through the
@@ -194,7 +179,7 @@ __device__ __forceinline__ int tile8_off(int row, int chunk) { return row * 128 
 // The lane byte offsets into the tile do not depend on the tile, so they
 // are computed once.
 //   row tile (64 rows x 256 B): rows (64/NW)*w + 4i + l/16, logical chunk
-//     (l%16) ^ swz(row) (the layout of tile_dma);
+//     (l%16) ^ swz(row) (the layout of tile_off);
 //   T tile (128 rows x 128 B): rows (128/NW)*w + 8i + l/8, logical chunk
 //     (l%8) ^ swz8(row).
 template <int NW>
@@ -238,22 +223,6 @@ __device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t* lds, int row, int
   return *reinterpret_cast<const bf16x8*>(lds + tile_off(row, chunk * 8));
 }
 
-// Transposed MFMA operand (32x32x16, A side): lane l gets column col0 + l%32
-// of rows {rbase + 4*(l/32) + e, rbase + 8 + 4*(l/32) + e : e = 0..3}, i.e. the
-// k ordering that matches the register layout of a 32x32 accumulator block
-// whose rows are these tile rows (see mfma_kperm below).  rbase % 16 == 0.
-__device__ __forceinline__ bf16x8 lds_col_frag(const uint16_t* lds, int rbase, int col0, int lane) {
-  const int g = lane >> 4;
-  const int row = rbase + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = col0 + 16 * (g & 1) + 4 * (lane & 3);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + tile_off(row, col)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + tile_off(row + 8, col)));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo);
-  const u32x2 b = __builtin_bit_cast(u32x2, hi);
-  const u32x4 v = {a[0], a[1], b[0], b[1]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // ---------------------------------------------------------------------------
 // MFMA 32x32x16 bf16 (fp32 accumulate).  Register layout (lane l, wave64):
 //   A[32 x 16]: lane holds A[l%32][8*(l/32) + t], t = 0..7
@@ -264,7 +233,7 @@ __device__ __forceinline__ bf16x8 lds_col_frag(const uint16_t* lds, int rbase, i
 // permuted: accumulator entries j = 8g .. 8g+7 of lane l hold rows
 // 16g + 8*(t/4) + 4*(l/32) + t%4 (t = j - 8g), which is k index 8*(l/32) + t
 // of a 16-deep step when row and k index differ by swapping bits 2 and 3.
-// lds_col_frag reads its 8 rows in exactly that order.
+// The T tiles store their tokens in exactly that order (lds_vt_frag).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -18,8 +18,8 @@ struct FwdParams {
   const int32_t* k_lens;    // [B] valid key counts or nullptr (all Lk)
   const int32_t* q_lens;    // [B] valid query counts or nullptr (all Lq); rows past it are not written
   int q_pos0, k_pos0;       // RoPE token index of query row 0 and key row 0 (shards of a longer sequence)
-  // Self-attention: k and v in the tile layout of launch_kv_tiles (then k/v
-  // above are unused), [B, H, ceil(Lk/64)] tiles; nullptr: read k/v directly.
+  // k and v in the tile layout of launch_kv_tiles (k/v above are then
+  // unused), [B, H, ceil(Lk/64)] tiles.
   const uint16_t* kt;       // keys, tiles of [64][128]: bf16, or with RoPE fp16 of R(p) k * 2^-e_t
   const int* kexp;          // with RoPE: e_t of every tile, else nullptr
   const uint16_t* vt;       // V^T, tiles of [128][64] bf16
@@ -86,9 +86,8 @@ struct MergeParams {
   int R, B, L, H;
 };
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
-hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
-// Self-attention over the prep pass's tiles (p.kt, p.vt, and p.kexp with RoPE); launch_attn_fwd
-// dispatches here when p.kt is set.
+// Attention over the prep pass's tiles (p.kt, p.vt, and p.kexp with RoPE): self-attention, its shards
+// and variable lengths, and cross-attention (Lq != Lk, p.k_lens, no RoPE).
 hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream);
 // FP8 forward: K as e4m3 row tiles [64][128] and V as e4m3 V^T tiles [128][64]
 // (8 KB each, key order kappa), with int32 exponents per tile.

@@ -297,7 +297,8 @@ int validate_cross_bwd(const void* q, const void* k, const void* v, const int32_
 }
 
 int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
-                       const float* lse, int B, int Lq, int Lk, int H, int D, float scale) {
+                       const float* lse, int B, int Lq, int Lk, int H, int D, float scale, const void* ws,
+                       size_t ws_bytes) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return WANATTN_ERR_NULL;
   WANATTN_TRY(check_dims(B, Lq, H, D));
   WANATTN_TRY(check_dims(B, Lk, H, D));
@@ -308,6 +309,8 @@ int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_
   WANATTN_TRY(check_bf16(o));
   if (lse != nullptr && !aligned(lse, 4)) return WANATTN_ERR_ALIGN;
   if (k_lens != nullptr && !aligned(k_lens, 4)) return WANATTN_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < fwd_tiles_ws_bytes(B, Lk, H, D, 0)) return WANATTN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return WANATTN_ERR_ALIGN;
   return WANATTN_OK;
 }
 

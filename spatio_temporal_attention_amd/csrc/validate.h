@@ -100,6 +100,7 @@ int validate_cross_bwd(const void* q, const void* k, const void* v, const int32_
                        const float* lse, const void* dout, const void* dq, const void* dk, const void* dv, int B,
                        int Lq, int Lk, int H, int D, float scale, const void* ws, size_t ws_bytes);
 int validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
-                       const float* lse, int B, int Lq, int Lk, int H, int D, float scale);
+                       const float* lse, int B, int Lq, int Lk, int H, int D, float scale, const void* ws,
+                       size_t ws_bytes);
 
 }  // namespace wanattn

@@ -61,6 +61,7 @@ H_API int h_validate_cross_bwd(const void* q, const void* k, const void* v, cons
   return validate_cross_bwd(q, k, v, k_lens, o, lse, dout, dq, dk, dv, B, Lq, Lk, H, D, scale, ws, ws_bytes);
 }
 H_API int h_validate_cross_fwd(const void* q, const void* k, const void* v, const int32_t* k_lens, const void* o,
-                               const float* lse, int B, int Lq, int Lk, int H, int D, float scale) {
-  return validate_cross_fwd(q, k, v, k_lens, o, lse, B, Lq, Lk, H, D, scale);
+                               const float* lse, int B, int Lq, int Lk, int H, int D, float scale, const void* ws,
+                               size_t ws_bytes) {
+  return validate_cross_fwd(q, k, v, k_lens, o, lse, B, Lq, Lk, H, D, scale, ws, ws_bytes);
 }

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libwanattn.so"
         assert n in wa._SIGNATURES, f"{n} has no binding"
@@ -173,16 +173,23 @@ def test_self_bwd_validation(lib):
 
 def test_cross_and_rope_validation(lib):
     def cross(**kw):
-        a = dict(q=P, k=P, v=P, kl=P, o=P, lse=P, B=2, Lq=100, Lk=512, H=2, D=128, scale=0.088)
+        a = dict(q=P, k=P, v=P, kl=P, o=P, lse=P, B=2, Lq=100, Lk=512, H=2, D=128, scale=0.088, ws=P,
+                 ws_bytes=1 << 30)
         a.update(kw)
         return lib.wanattn_cross_fwd(a["q"], a["k"], a["v"], a["kl"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"],
-                                     a["H"], a["D"], a["scale"], None)
+                                     a["H"], a["D"], a["scale"], a["ws"], a["ws_bytes"], None)
     assert cross(v=None) == NULL
     assert cross(Lk=0) == SHAPE
     assert cross(Lq=-5) == SHAPE
     assert cross(D=127) == UNSUP
     assert cross(kl=P + 1) == ALIGN
     assert cross(scale=float("nan")) == UNSUP
+    need = lib.wanattn_cross_fwd_workspace_bytes(2, 512, 2, 128)
+    assert need == 2 * (2 * 2 * 8 * 64 * 128 * 2)                       # K and V^T tiles, 8 per (b, h)
+    assert lib.wanattn_cross_fwd_workspace_bytes(1, 336, 40, 128) == 2 * 40 * 6 * 64 * 128 * 2
+    assert cross(ws=None) == WS
+    assert cross(ws_bytes=need - 1) == WS
+    assert cross(ws=ODD) == ALIGN
 
     def rope(**kw):
         a = dict(x=P, y=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P, inv=0)

@@ -51,7 +51,7 @@ SIGS = {
     "h_validate_lse_merge": (_i, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i, _vp, _vp, _i, _i, _i, _i]),
     "h_validate_self_bwd": (_i, [_vp] * 9 + [_i] * 4 + [Grid, Rope, _vp, _f, _vp, _sz]),
     "h_validate_cross_bwd": (_i, [_vp] * 10 + [_i] * 5 + [_f, _vp, _sz]),
-    "h_validate_cross_fwd": (_i, [_vp] * 6 + [_i] * 5 + [_f]),
+    "h_validate_cross_fwd": (_i, [_vp] * 6 + [_i] * 5 + [_f, _vp, _sz]),
 }
 
 
@@ -229,9 +229,14 @@ def test_validate_backward_and_cross(h):
     assert c(*cptr, 2, 1000, 0, 3, 128, 0.088, buf(11), cws) == SHAPE
     assert c(*cptr, 2, 1000, 512, 3, 128, 0.088, buf(11), cws - 1) == WS
     x = h.h_validate_cross_fwd
-    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088) == OK
-    assert x(buf(1), buf(2), buf(3), None, buf(5), None, 2, 32760, 512, 12, 128, 0.088) == OK
-    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 0, 12, 128, 0.088) == SHAPE
-    assert x(buf(1), None, buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088) == NULL
-    assert x(buf(1), buf(2), buf(3), buf(4, 1), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088) == ALIGN
-    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, math.inf) == UNSUP
+    xws = h.h_fwd_tiles_ws_bytes(2, 512, 12, 128, 0)
+    w = (buf(7), xws)
+    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088, *w) == OK
+    assert x(buf(1), buf(2), buf(3), None, buf(5), None, 2, 32760, 512, 12, 128, 0.088, *w) == OK
+    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 0, 12, 128, 0.088, *w) == SHAPE
+    assert x(buf(1), None, buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088, *w) == NULL
+    assert x(buf(1), buf(2), buf(3), buf(4, 1), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088, *w) == ALIGN
+    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, math.inf, *w) == UNSUP
+    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088, None, xws) == WS
+    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088, buf(7), xws - 1) == WS
+    assert x(buf(1), buf(2), buf(3), buf(4), buf(5), buf(6), 2, 32760, 512, 12, 128, 0.088, buf(7, 8), xws) == ALIGN
