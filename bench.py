@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (profiling runs)")
     ap.add_argument("--no-extras", action="store_true", help="skip the varlen / ring-shard / merge measurements")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload forward timings and the MFMA loop (profiling runs of the step)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the per-workload forward timings and the MFMA loop (profiling runs of those)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain device copy of known size (for scaling HBM counters)")
     return ap.parse_args()
@@ -221,10 +225,11 @@ def bench_configs(wa, torch, synth, dev, rope, peak_meas, c4_ms):
     del q, k, v, o, lse
     torch.cuda.empty_cache()
     w = synth.WORKLOADS[4]
-    out["C4"] = dict(workload=f"720p: self-attention forward, grid 21x45x80 (L={w.L}), B=1, H=40, D=128, 3D RoPE "
-                              f"(the headline; median over the timed steps)",
-                     **_rate(4.0 * w.H * w.L * w.L * w.D, c4_ms, peak_meas))
-    return {k: out[k] for k in ("C1", "C2", "C3", "C4", "C5")}
+    if c4_ms is not None:
+        out["C4"] = dict(workload=f"720p: self-attention forward, grid 21x45x80 (L={w.L}), B=1, H=40, D=128, "
+                                  f"3D RoPE (the headline; median over the timed steps)",
+                         **_rate(4.0 * w.H * w.L * w.L * w.D, c4_ms, peak_meas))
+    return {k: out[k] for k in ("C1", "C2", "C3", "C4", "C5") if k in out}
 
 
 def bench_next_rows(wa, torch, synth, dev, rope):
@@ -328,9 +333,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n}))
         return
 
+    rope = wa.RopeConfig(48, 40, 40, 10000.0)
+    if args.configs_only:
+        peak = measure_mfma_peak(wa)
+        print(json.dumps({"mfma_peak_measured": peak,
+                          "configs": bench_configs(wa, torch, synth, dev, rope, peak["tflops"], None)}), flush=True)
+        return
     w = synth.WORKLOADS[4]
     B, L, H, D = w.B, w.L, w.H, w.D
-    rope = wa.RopeConfig(48, 40, 40, 10000.0)
     scale = 1.0 / math.sqrt(D)
     t0 = time.perf_counter()
     inp = synth.make_inputs(4, rows_per_head=CPU_SAMPLE_ROWS)
@@ -449,7 +459,7 @@ def main():
     if not args.fwd_only and not args.no_extras:
         result["next_rows"] = bench_next_rows(wa, torch, synth, dev, rope)
         log("next rows done")
-    if not args.fwd_only:
+    if not args.fwd_only and not args.no_configs:
         del q, k, v, do, o, xo, dq, dk, dv, ws_f, ws_b, ws_x
         torch.cuda.empty_cache()
         peak = measure_mfma_peak(wa)
