@@ -175,8 +175,9 @@ int wanattn_self_fwd_fp8(const void* q, const void* k, const void* v, void* o, f
  *   dq_i = R(p_i)^T scale sum_j dS_ij R(p_j) k_j;  dk_j = R(p_j)^T scale sum_i dS_ij R(p_i) q_i.
  * Gradients are with respect to the unrotated q and k.  table == NULL: no RoPE.
  * Workspace (required, 16-byte aligned): wanattn_self_bwd_workspace_bytes bytes
- * (the same with or without a table).  It receives Delta (fp32 [B, H, L]) and
- * 64-token tiles of every (b, h): q and k (rotated with a table) in fp16 with
+ * (the same with or without a table).  It receives, per 64-token query tile
+ * of every (b, h), the row statistics LSE_i * log2(e) and -Delta_i (fp32,
+ * 1 KB a tile) and 64-token tiles of every (b, h): q and k (rotated with a table) in fp16 with
  * the forward's per-tile powers of two, their bf16 transposes, dout (rows and
  * transposed) and v, so that P is recomputed from exactly the operands the
  * forward multiplied; when few key blocks would leave the GPU idle (a short

@@ -275,7 +275,8 @@ namespace {
 
 // Backward over q-side [B, Lq, H, D] and k-side [B, Lk, H, D] tensors: prep
 // passes (Q and K, rotated with a table, as fp16 tiles with the forward's
-// power-of-two exponents, their bf16 transposes, dO and V tiles, Delta), then
+// power-of-two exponents, their bf16 transposes, dO and V tiles, the row
+// statistics LSE * log2 e and -Delta), then
 // the dK/dV and dQ passes over those tiles.  k_lens: key padding or nullptr.
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
             void* dk, void* dv, const int32_t* k_lens, int B, int Lq, int Lk, int H, int D, const RopeDev& rope,
@@ -293,7 +294,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.kt = (const uint16_t*)(base + w.kt);
   p.vr = (const uint16_t*)(base + w.vr);
   p.lse = lse;
-  p.delta = (const float*)(base + w.delta);
+  p.qstat = (const float*)(base + w.qstat);
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
@@ -313,9 +314,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
                                         (int*)(base + w.kexp), (uint16_t*)(base + w.kt), (uint16_t*)(base + w.vr), B,
                                         Lk, H, rope, k_lens, s));
   if (e != WANATTN_OK) return e;
-  e = hip_status(launch_bwd_q_tiles((const uint16_t*)q, (const uint16_t*)dout, (const uint16_t*)o,
+  e = hip_status(launch_bwd_q_tiles((const uint16_t*)q, (const uint16_t*)dout, (const uint16_t*)o, lse,
                                     (uint16_t*)(base + w.qf), (int*)(base + w.qexp), (uint16_t*)(base + w.qt),
-                                    (uint16_t*)(base + w.dor), (uint16_t*)(base + w.dot), (float*)(base + w.delta), B,
+                                    (uint16_t*)(base + w.dor), (uint16_t*)(base + w.dot), (float*)(base + w.qstat), B,
                                     Lq, H, rope, s));
   if (e != WANATTN_OK) return e;
   e = hip_status(launch_bwd_dkdv(p, s));

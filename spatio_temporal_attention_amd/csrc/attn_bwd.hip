@@ -30,6 +30,7 @@
 //    dP^T = V dO^T (lane owns query i), dQ~^T += (R k)^T dS^T.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "bwd_common.h"
 #include "validate.h"
@@ -41,22 +42,53 @@ namespace {
 using namespace bwd;
 
 // dk~_j = scale sum_i dS_ij q~_i, dS_ij = P_ij (<dO_i, v_j> - Delta_i).
-// Workgroup = 256 keys (8 waves, one workgroup per CU); query tiles staged
-// as Q fp16 rows, dO rows and (R q)^T.  S = Q K^T and dP - Delta = dO V^T -
-// Delta (the accumulator starts at -Delta of its rows) from the wave's K
-// and V rows in registers; dK~^T += (R q)^T dS with dS from the accumulators.
+// Workgroup = 256 keys (8 waves, one workgroup per CU, two waves per SIMD);
+// query tiles staged as Q fp16 rows, dO rows, (R q)^T and the row
+// statistics.  A wave holds the K and V rows of its 32 keys in registers (the
+// B operands of S = Q K^T and of dP - Delta = dO V^T - Delta, whose
+// accumulator starts at -Delta) and accumulates dK~^T += (R q)^T dS with dS
+// taken from the accumulators.  A lane holds 16 query rows of each 32-row
+// block; their statistics reach it from the lane of its 16-lane row that
+// read them (DPP row broadcast), so one 16-byte LDS read per lane and tile
+// carries them all.
+//
+// Ping-pong, as in the forward: each wave alternates a products phase M(u)
+// (MFMA: dK~ += (R q)^T dS of query tile u-1, then S and dP of tile u) and a
+// softmax phase V(u) (VALU: P and dS of tile u); waves 4..7 run one phase
+// behind waves 0..3 and all eight meet at a barrier after every phase, so on
+// each SIMD (waves w and w + 4) one wave feeds the matrix cores while the
+// other computes its dS.
+//
+// Interval k lies between barriers k-1 and k; the early waves run phase k
+// (M(u) = 2u, V(u) = 2u+1) in interval k, the late waves in interval k+1.
+// Q/dO of tile u are read in intervals 2u..2u+1, its statistics in
+// 2u..2u+2, its (R q)^T in 2u+2..2u+3 (double buffers; statistics in a ring
+// of four).  In interval 2u every wave copies its share of Q/dO(u+1) and
+// (R q)^T(u), wave 0 the statistics of u+1 (the early waves at the start of
+// M(u), the late ones at the start of V(u-1)), into slots last read in
+// interval 2u-1 or before; each wave waits for its copies before barrier
+// 2u+1, and they are first read in interval 2u+2: two intervals of latency.
+constexpr uint32_t DK_QD = 0;        // Q row tile at + 32768 * slot, dO row tile at + 16384
+constexpr uint32_t DK_QT = 65536;    // (R q)^T at + 16384 * slot
+constexpr uint32_t DK_ST = 98304;    // statistics at + 1024 * (tile & 3)
+constexpr uint32_t DK_LDS = DK_ST + 4 * 1024;
+static_assert(QSTAT_FLOATS * 4 == 1024, "one 1 KB copy per statistics tile");
+
+// out[j] = x of lane j of this lane's 16-lane row (DPP row_newbcast:j).
+template <int... J>
+__device__ __forceinline__ void row_bcast16_impl(float x, float* out, std::integer_sequence<int, J...>) {
+  ((out[J] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf,
+                                                                   0xf, false))),
+   ...);
+}
+__device__ __forceinline__ void row_bcast16(float x, float (&out)[16]) {
+  row_bcast16_impl(x, out, std::make_integer_sequence<int, 16>{});
+}
+
 template <bool KMASK, bool TAIL>
-__global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse2_s0[TILE_ROWS];   // LSE * log2 e (+inf: no row)
-  __shared__ __attribute__((aligned(16))) float lse2_s1[TILE_ROWS];
-  __shared__ __attribute__((aligned(16))) float ndelta_s0[TILE_ROWS];   // -Delta
-  __shared__ __attribute__((aligned(16))) float ndelta_s1[TILE_ROWS];
+__global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dk_kernel(
+    BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DK_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -64,6 +96,7 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool late = wv >= DK_WAVES / 2;   // waves 4..7: one phase behind
   const KeySide ks = key_side<DK_WAVES, KMASK, TAIL>(p, wv, col);
 
   bf16x8 kf[8], vf[8];   // K fp16 (bit patterns), V bf16: B operands of S and dP
@@ -75,8 +108,19 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
   f32x16 dk_acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) dk_acc[d] = f32x16{};
-  const float* lse_row = p.lse + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
-  const float* delta_row = p.delta + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
+
+  // This lane's LDS byte offsets; the slot, the 32-row block and the matrix
+  // are immediates.  Row fragments (Q, dO): row col, chunk 2s + half
+  // (tile_off's swizzle); (R q)^T fragments: row col, chunk 2kg + half
+  // (tile8_off's); statistics: entry 16 half + lane % 16.
+  uint32_t rf[8], tf[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) rf[s] = DK_QD + col * 256 + (((2 * s + half) ^ swz(col)) << 4);
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) tf[kg] = DK_QT + col * 128 + (((2 * kg + half) ^ swz8(col)) << 4);
+  const uint32_t sf = DK_ST + 16 * (16 * half + (lane & 15));
+  auto frag = [&](uint32_t off) { return *reinterpret_cast<const bf16x8*>(smem + off); };
+  auto stat4 = [&](uint32_t off) { return *reinterpret_cast<const f32x4*>(smem + off); };
 
   uint32_t roff[2], toff[2];
 #pragma unroll
@@ -88,122 +132,151 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) void bwd_dk_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + ks.tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t dor = tile_rsrc(p.dor + ks.tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t qtr = tile_rsrc(p.qt + ks.tile0 * TILE_ELEMS, bytes);
-  const_i32* qexp = const_ptr(p.qexp + ks.tile0);   // scalar loads
-
-  struct Buf {
-    uint16_t* q;
-    uint16_t* dO;
-    uint16_t* qt;
-    float* lse2;
-    float* ndelta;
-  };
-  const Buf buf0{q_lds0, do_lds0, qt_lds0, lse2_s0, ndelta_s0};
-  const Buf buf1{q_lds1, do_lds1, qt_lds1, lse2_s1, ndelta_s1};
-  auto stage = [&](const Buf& dst, int t) {
+  const __amdgpu_buffer_rsrc_t str = tile_rsrc(p.qstat + ks.tile0 * QSTAT_FLOATS, (uint32_t)ks.nt * 1024u);
+  auto copy_qd = [&](int slot, int t) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      buf_dma16(qfr, roff[i], soff, tile_lds_block<DK_WAVES>(dst.q, wv, i));
-      buf_dma16(dor, roff[i], soff, tile_lds_block<DK_WAVES>(dst.dO, wv, i));
-      buf_dma16(qtr, toff[i], soff, tile_lds_block<DK_WAVES>(dst.qt, wv, i));
+      buf_dma16(qfr, roff[i], soff, smem + DK_QD + 32768 * slot + 2048 * wv + 1024 * i);
+      buf_dma16(dor, roff[i], soff, smem + DK_QD + 32768 * slot + 16384 + 2048 * wv + 1024 * i);
     }
   };
-  // Row statistics of query tile t: threads 0..63 read LSE, 64..127 Delta,
-  // into a register, published to LDS once loaded.
-  auto load_stats = [&](int t) {
-    float x = 0.f;
-    if (tid < TILE_ROWS) {
-      const int i = t * TILE_ROWS + tid;
-      x = (i < p.Lq) ? lse_row[i] : -INFINITY;
-    } else if (tid < 2 * TILE_ROWS) {
-      const int i = t * TILE_ROWS + tid - TILE_ROWS;
-      x = (i < p.Lq) ? delta_row[i] : 0.f;
-    }
-    return x;
+  auto copy_qt = [&](int slot, int t) {
+    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buf_dma16(qtr, toff[i], soff, smem + DK_QT + 16384 * slot + 2048 * wv + 1024 * i);
   };
-  auto store_stats = [&](const Buf& dst, float x) {
-    // rows past Lq, and rows with no valid key (LSE = -inf), contribute nothing
-    if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
-    else if (tid < 2 * TILE_ROWS) dst.ndelta[tid - TILE_ROWS] = -x;
+  auto copy_stats = [&](int t) {
+    if (wv == 0) buf_dma16(str, 16 * lane, (uint32_t)t * 1024u, smem + DK_ST + 1024 * (t & 3));
   };
 
   // A query split can be empty (rounding of the split size): it writes zero partials.
-  if (ks.t0 < ks.t1) {
-    int e_q;
-    {
-      const float st = load_stats(ks.t0);
-      stage(buf0, ks.t0);
-      e_q = qexp[ks.t0];
-      wait_vmem();
-      store_stats(buf0, st);
-    }
-    __syncthreads();
-
-    auto iteration = [&](auto parity, int t) {
-      constexpr int P = decltype(parity)::value;
-      const Buf& cur = P ? buf1 : buf0;
-      const Buf& nxt = P ? buf0 : buf1;
-      const bool has_next = t + 1 < ks.t1;
-      int e_q_next = 0;
-      float st = 0.f;
-      if (has_next) {
-        st = load_stats(t + 1);
-        stage(nxt, t + 1);
-        e_q_next = qexp[t + 1];
+  const int n = ks.t1 - ks.t0;
+  if (n > 0) {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // The copies of interval 2u (tile u = index within the range): Q/dO(u+1) into slot
+    // (u+1) & 1, (R q)^T(u) into slot u & 1, statistics(u+1).
+    auto copies = [&](auto parity, int u) {
+      constexpr int P = decltype(parity)::value;   // u & 1
+      if (u + 1 < n) {
+        copy_qd(P ^ 1, ks.t0 + u + 1);
+        copy_stats(ks.t0 + u + 1);
       }
-      // With a key mask, a wave whose 32 keys are all padding skips the products
-      // (its gradients stay zero) but still copies its share and meets every barrier.
-      if (!KMASK || ks.wave_live) {
-      const float g = ldexpf(p.scale_log2, e_q + e_k);
-      bf16x8 dsf[4];
-  #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
-        f32x16 s_acc = f32x16{}, dp_acc;
-  #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 nd = *reinterpret_cast<const f32x4*>(cur.ndelta + qb * 32 + 8 * m + 4 * half);
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) dp_acc[4 * m + e] = nd[e];
-        }
-  #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-          dp_acc = mfma32(lds_row_frag(cur.dO, qb * 32 + col, 2 * s + half), vf[s], dp_acc);
-        }
-        float dsv[16];
-  #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
-            if (KMASK && !ks.key_live) pe = 0.f;
-            dsv[4 * m + e] = pe * dp_acc[4 * m + e];
-          }
-        }
-        dsf[2 * qb] = pack_acc8(dsv);
-        dsf[2 * qb + 1] = pack_acc8(dsv + 8);
-      }
-  #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-  #pragma unroll
-        for (int qg = 0; qg < 4; ++qg) dk_acc[d] = mfma32(lds_vt_frag(cur.qt, d * 32 + col, qg, half), dsf[qg], dk_acc[d]);
-      }
-      }
-      if (has_next) {
-        wait_vmem();
-        store_stats(nxt, st);
-      }
-      __syncthreads();
-      e_q = e_q_next;
+      copy_qt(P, ks.t0 + u);
     };
-    int t = ks.t0;
-    for (; t + 1 < ks.t1; t += 2) {
-      iteration(std::integral_constant<int, 0>{}, t);
-      iteration(std::integral_constant<int, 1>{}, t + 1);
+    copy_qd(0, ks.t0);
+    copy_stats(ks.t0);
+    wait_vmem();
+    __syncthreads();
+    if (late) {
+      copies(P0{}, 0);   // interval 0: the late waves' "V(-1)"
+      dma_barrier();     // the early waves run M(0) meanwhile
     }
-    if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
+
+    f32x16 s_acc[2], dp_acc[2];
+    bf16x8 dsf[4];
+    // The end of a phase (VMEM: wait for this wave's copies first).  No
+    // instruction moves across it: each phase keeps to its own pipe.
+    auto phase_end = [&](bool vmem) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (vmem) wait_vmem();
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // M(u), parity P = u & 1: dK~ of tile u-1 (GRAD: u > 0), then S and dP of tile u (SDP: u < n).
+    auto m_phase = [&](auto parity, auto grad_tag, auto sdp_tag, int u) {
+      constexpr int P = decltype(parity)::value;
+      constexpr bool GRAD = decltype(grad_tag)::value;
+      constexpr bool SDP = decltype(sdp_tag)::value;
+      const int t = ks.t0 + u;
+      if (SDP && !late) copies(parity, u);
+      if (!KMASK || ks.wave_live) {
+        if (GRAD) {
+#pragma unroll
+          for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              dk_acc[d] = mfma32(frag(tf[kg] + 16384 * (P ^ 1) + 4096 * d), dsf[kg], dk_acc[d]);
+        }
+        if (SDP) {
+          // -Delta of the accumulator's rows: {LSE log2 e, -Delta} x 2 blocks per entry
+          const f32x4 st = stat4(sf + 1024 * (t & 3));
+          float nd[2][16];
+          row_bcast16(st[1], nd[0]);
+          row_bcast16(st[3], nd[1]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            s_acc[qb] = f32x16{};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) dp_acc[qb][j] = nd[qb][j];
+          }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              s_acc[qb] = mfma32_f16(frag(rf[s] + 32768 * P + 8192 * qb), kf[s], s_acc[qb]);
+              dp_acc[qb] = mfma32(frag(rf[s] + 32768 * P + 16384 + 8192 * qb), vf[s], dp_acc[qb]);
+            }
+        }
+        // Keep four fragment reads in flight ahead of the MFMAs.
+        constexpr int n_mfma = (GRAD ? 16 : 0) + (SDP ? 32 : 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < n_mfma - 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      phase_end(late);
+    };
+    // V(u): P = exp2(S g - LSE log2 e), dS = P (dP - Delta), packed to bf16 for the next M.
+    auto v_phase = [&](auto parity, int u) {
+      const int t = ks.t0 + u;
+      if (late && u + 1 < n) copies(std::integral_constant<int, decltype(parity)::value ^ 1>{}, u + 1);
+      if (!KMASK || ks.wave_live) {
+        const f32x4 st = stat4(sf + 1024 * (t & 3));
+        const int e_q = *reinterpret_cast<const int*>(smem + DK_ST + 1024 * (t & 3) + 512);
+        const float g = ldexpf(p.scale_log2, e_q + e_k);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float l2[16], dsv[16];
+          row_bcast16(qb ? st[2] : st[0], l2);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[qb][j], g, -l2[j]));
+            if (KMASK && !ks.key_live) pe = 0.f;
+            dsv[j] = pe * dp_acc[qb][j];
+          }
+          dsf[2 * qb] = pack_acc8(dsv);
+          dsf[2 * qb + 1] = pack_acc8(dsv + 8);
+          __builtin_amdgcn_sched_barrier(0);   // one 32-row half at a time (registers)
+        }
+        // dS is complete here: the code sinking passes must not move its
+        // arithmetic past the barrier into the next products phase.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin_vgprs(dsf[i]);
+      }
+      phase_end(!late);
+    };
+    m_phase(P0{}, std::false_type{}, std::true_type{}, 0);
+    v_phase(P0{}, 0);
+    int u = 1;
+    for (; u + 1 < n; u += 2) {
+      m_phase(P1{}, std::true_type{}, std::true_type{}, u);
+      v_phase(P1{}, u);
+      m_phase(P0{}, std::true_type{}, std::true_type{}, u + 1);
+      v_phase(P0{}, u + 1);
+    }
+    if (u < n) {
+      m_phase(P1{}, std::true_type{}, std::true_type{}, u);
+      v_phase(P1{}, u);
+    }
+    // M(n): the last tile's dK~ product
+    if (n & 1) m_phase(P1{}, std::true_type{}, std::false_type{}, n);
+    else m_phase(P0{}, std::true_type{}, std::false_type{}, n);
+    if (!late) dma_barrier();   // matches the late waves' barrier before their M(0)
   }
 
   if (TAIL) {
@@ -349,10 +422,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   load_row_frags(qf, p.qf + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
   load_row_frags(dof, p.dor + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
   const int e_q = tile_ok ? p.qexp[tile0 + qtile] : 0;
-  const int64_t stat = ((int64_t)b * p.H + h) * p.Lq + i;
-  const float lse_i = row_ok ? p.lse[stat] : -INFINITY;
-  const float lse2 = (lse_i > -INFINITY) ? lse_i * LOG2E : INFINITY;   // no valid key: P = 0
-  const float delta = row_ok ? p.delta[stat] : 0.f;
+  // LSE_i log2 e (+inf past Lq or with no valid key: P = 0) and -Delta_i, from the query prep pass
+  // (row r = 32 (wave % 2) + col of the tile sits in entry 16 ((r / 4) % 2) + 4 ((r / 8) % 4) + r % 4)
+  const float* st = p.qstat + (tile0 + (tile_ok ? qtile : 0)) * QSTAT_FLOATS +
+                    4 * (16 * ((col >> 2) & 1) + 4 * ((col >> 3) & 3) + (col & 3)) + 2 * (wave & 1);
+  const float lse2 = tile_ok ? st[0] : INFINITY;
+  const float ndelta = tile_ok ? st[1] : 0.f;
 
   f32x16 dq_acc[4];
 #pragma unroll
@@ -412,7 +487,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
           const int key = t * TILE_ROWS + kb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
           if (key >= n_keys) pe = 0.f;
         }
-        dsv[jj] = pe * (dp_acc[jj] - delta);
+        dsv[jj] = pe * (dp_acc[jj] + ndelta);
       }
       dsf[2 * kb] = pack_acc8(dsv);
       dsf[2 * kb + 1] = pack_acc8(dsv + 8);

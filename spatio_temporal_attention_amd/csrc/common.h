@@ -18,6 +18,10 @@ namespace wanattn {
 constexpr int HD = 128;               // head dim (the only one supported)
 constexpr int TILE_ROWS = 64;         // rows of one staged tile
 constexpr int TILE_ELEMS = TILE_ROWS * HD;
+// Backward row statistics of one query tile (1 KB): LSE_i * log2(e) and
+// -Delta_i of its 64 rows in the accumulators' row order (512 bytes), then the
+// tile's exponent e_q (int bits), then zeros.
+constexpr int QSTAT_FLOATS = 4 * TILE_ROWS;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -165,6 +169,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier for kernels whose LDS is written only by DMA copies: the
+// wave's own LDS reads have returned (lgkmcnt 0), copies still in flight are
+// not waited for (callers wait for those with wait_vmem() before the barrier
+// that publishes them), and the compiler keeps memory accesses on their side
+// of it.  (A release/acquire fence would add a wait for every copy in flight.)
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Tiles of 128-byte rows: the fp8 key tile (64 keys x 128 d, 8 KB) and the
 // V^T tile (128 d x 64 keys in bf16, 16 KB).  The 8 16-byte chunks of row r
 // sit at chunk c ^ swz8(r), swz8(r) = (r >> 1) & 7: the 16 rows a 16-lane
@@ -202,6 +218,14 @@ __device__ __forceinline__ uint8_t* tile_lds_block(void* lds_tile, int wave, int
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// An empty asm statement that reads and rewrites x in place: x is computed
+// before this point and nothing that produces it moves below it.
+__device__ __forceinline__ void pin_vgprs(bf16x8& x) {
+  u32x4 w = __builtin_bit_cast(u32x4, x);
+  asm volatile("" : "+v"(w));
+  x = __builtin_bit_cast(bf16x8, w);
+}
+
 // One 1 KB copy: 64 lanes x 16 bytes from base + soff + voff into lds_block.
 __device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_block) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, soff, 0,

@@ -46,7 +46,7 @@ struct BwdParams {
   const uint16_t* kt;       // (R k)^T T tiles, bf16
   const uint16_t* vr;       // V row tiles, bf16
   const float* lse;         // [B, H, L]
-  const float* delta;       // [B, H, L]
+  const float* qstat;       // per query tile [B, H, nt][QSTAT_FLOATS]: LSE_i * log2(e), then -Delta_i
   uint16_t* dq;             // [B, L, H, 128] bf16 outputs
   uint16_t* dk;
   uint16_t* dv;
@@ -98,9 +98,9 @@ hipError_t launch_attn_fwd_fp8(const FwdParams& p, const uint8_t* k8, const int*
 hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf, int* kexp, uint16_t* kt,
                               uint16_t* vr, int B, int L, int H, const RopeDev& rope, const int32_t* lens,
                               hipStream_t stream);
-hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
-                              uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
-                              const RopeDev& rope, hipStream_t stream);
+hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, const float* lse,
+                              uint16_t* qf, int* qexp, uint16_t* qt, uint16_t* dor, uint16_t* dot, float* qstat, int B,
+                              int L, int H, const RopeDev& rope, hipStream_t stream);
 // The dV pass alone (attn_bwd_dv.hip), p.n_tiles = key blocks of 256; called by launch_bwd_dkdv
 // with the workgroup counts of the main launch and of the tail split's launch (0: none).
 hipError_t launch_bwd_dv(const BwdParams& p, int n_main, int n_tail, hipStream_t stream);

@@ -19,7 +19,8 @@
 // Backward (bwd_k_tiles_kernel, bwd_q_tiles_kernel): the fp16 tiles of K and
 // Q with their exponents (bit-identical to what the forward multiplies, so
 // the recomputed scores match the forward's LSE), T tiles of R(p)k, R(p)q
-// and dO, row tiles of V and dO, and Delta_i = <dO_i, O_i>.
+// and dO, row tiles of V and dO, and per query tile the row statistics
+// LSE_i * log2(e) and -Delta_i, Delta_i = <dO_i, O_i>.
 #include "common.h"
 #include "kernels.h"
 
@@ -202,16 +203,23 @@ __global__ __launch_bounds__(256) void bwd_k_tiles_kernel(const uint16_t* __rest
   store_row_tile_bf16(vr + off, f, tid);
 }
 
-// Backward, query side: Q fp16 tile + exponent, (R q)^T, dO rows, dO^T, Delta.
+// Backward, query side: Q fp16 tile + exponent, (R q)^T, dO rows, dO^T, and the tile's row
+// statistics: LSE * log2(e) (+inf for a row past L or without a valid key: P = 0) and -Delta
+// (0 past L) in the order the backward's accumulators hold their rows, then the tile's exponent.
+// Entry x = 16 hf + j (x < 32) holds rows r and 32 + r, r = 8 (j / 4) + 4 hf + j % 4: the row of
+// register j of a 32x32 accumulator block in lane half hf, as {LSE log2 e (r), -Delta (r),
+// LSE log2 e (32 + r), -Delta (32 + r)}.
 __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ dout,
-                                                          const uint16_t* __restrict__ o, uint16_t* __restrict__ qf,
+                                                          const uint16_t* __restrict__ o,
+                                                          const float* __restrict__ lse, uint16_t* __restrict__ qf,
                                                           int* __restrict__ qexp, uint16_t* __restrict__ qt,
                                                           uint16_t* __restrict__ dor, uint16_t* __restrict__ dot,
-                                                          float* __restrict__ delta, int L, int H, int nt,
+                                                          float* __restrict__ qstat, int L, int H, int nt,
                                                           RopeDev rope) {
   __shared__ __attribute__((aligned(16))) StageRows s;
   __shared__ float wmax[4];
+  __shared__ float ndelta_s[TILE_ROWS];
   const int tile = blockIdx.x % nt;
   const int bh = blockIdx.x / nt;
   const int h = bh % H;
@@ -248,10 +256,25 @@ __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __rest
     d += __shfl_xor(d, 2, 16);
     d += __shfl_xor(d, 1, 16);
     const int n = tile * TILE_ROWS + frag_token(tid, it);
-    if (frag_chunk(tid) == 0 && n < L) delta[((int64_t)b * H + h) * L + n] = d;
+    if (frag_chunk(tid) == 0) ndelta_s[frag_token(tid, it)] = (n < L) ? -d : 0.f;
   }
   lds_barrier();
   store_t_tile(dot + off, s, tid);
+  float* st = qstat + (int64_t)blockIdx.x * QSTAT_FLOATS;
+  if (tid < 32) {
+    const int r = 8 * ((tid & 15) >> 2) + 4 * (tid >> 4) + (tid & 3);
+    f32x4 w;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int n = tile * TILE_ROWS + 32 * qb + r;
+      const float x = (n < L) ? lse[((int64_t)b * H + h) * L + n] : -INFINITY;
+      w[2 * qb] = (x > -INFINITY) ? x * 1.4426950408889634f : INFINITY;
+      w[2 * qb + 1] = ndelta_s[32 * qb + r];
+    }
+    *reinterpret_cast<f32x4*>(st + 4 * tid) = w;
+  } else if (tid >= 2 * TILE_ROWS) {
+    st[tid] = (tid == 2 * TILE_ROWS) ? __int_as_float(e) : 0.f;
+  }
 }
 
 hipError_t grid_of_tiles(int B, int L, int H, int& nt, dim3& grid) {
@@ -290,14 +313,14 @@ hipError_t launch_bwd_k_tiles(const uint16_t* k, const uint16_t* v, uint16_t* kf
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, uint16_t* qf, int* qexp,
-                              uint16_t* qt, uint16_t* dor, uint16_t* dot, float* delta, int B, int L, int H,
-                              const RopeDev& rope, hipStream_t stream) {
+hipError_t launch_bwd_q_tiles(const uint16_t* q, const uint16_t* dout, const uint16_t* o, const float* lse,
+                              uint16_t* qf, int* qexp, uint16_t* qt, uint16_t* dor, uint16_t* dot, float* qstat, int B,
+                              int L, int H, const RopeDev& rope, hipStream_t stream) {
   int nt;
   dim3 grid;
   if (grid_of_tiles(B, L, H, nt, grid) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_q_tiles_kernel, grid, dim3(256), 0, stream, q, dout, o, qf, qexp, qt, dor, dot, delta, L, H,
-                     nt, rope);
+  hipLaunchKernelGGL(bwd_q_tiles_kernel, grid, dim3(256), 0, stream, q, dout, o, lse, qf, qexp, qt, dor, dot, qstat, L,
+                     H, nt, rope);
   return hipGetLastError();
 }
 

@@ -121,8 +121,8 @@ BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {
   const size_t qbytes = qtiles * 64 * (size_t)D * 2;
   const size_t kbytes = ktiles * 64 * (size_t)D * 2;
   size_t at = 0;
-  w.delta = at;
-  at = align256(at + (size_t)B * H * Lq * 4);
+  w.qstat = at;
+  at = align256(at + qtiles * 1024);
   size_t* qparts[] = {&w.qf, &w.qt, &w.dor, &w.dot};
   for (size_t* part : qparts) {
     *part = at;

@@ -55,18 +55,19 @@ struct Fp8WsLayout {
   size_t k8, v8, kexp, vexp, total;
 };
 Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D);
-// Backward workspace: Delta (fp32 [B, H, L]), then the prep passes' tiles
+// Backward workspace: the row statistics of every query tile (fp32
+// [B, H, ceil(L/64)][256]: LSE * log2 e, -Delta, the tile exponent), then the prep passes' tiles
 // (each [B, H, ceil(L/64)] x 16 KB), the two exponent arrays (int32 per
 // tile) and, when the dK/dV passes split the query range (q_split > 1), their
 // fp32 partials (2 x q_split x [B, H, Lk, D]); each part starts on a 256-byte
 // boundary.
 struct BwdWsLayout {
-  size_t delta, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, part, kv_part, dq_part, total;
+  size_t qstat, qf, qt, dor, dot, kf, kt, vr, qexp, kexp, part, kv_part, dq_part, total;
   int q_split;
   FwdSplit kv_split;   // tail split of the dK/dV passes (256-key blocks; only without a query split)
   FwdSplit dq_split;   // tail split of the dQ pass (256-row query blocks, the forward's rule)
 };
-// Query-side parts (Delta, qf, qt, dor, dot, qexp) over Lq tokens, key-side
+// Query-side parts (qstat, qf, qt, dor, dot, qexp) over Lq tokens, key-side
 // parts (kf, kt, vr, kexp) over Lk.
 // Query-range split of the dK/dV passes: 1 while the key blocks alone give at
 // least 256 workgroups, else enough splits for ~512 (each >= 8 query tiles, at

@@ -80,16 +80,17 @@ def test_workspace_sizes(lib):
     assert lib.wanattn_self_fwd_workspace_bytes(1, 2048, 127, D, 0) == 2 * 127 * 2048 * D * 2     # 1,016 tiles
     # 1,040 tiles: the last 16 split 8 ways
     assert lib.wanattn_self_fwd_workspace_bytes(1, 2048, 130, D, 0) == 2 * 130 * 2048 * D * 2 + 16 * 8 * 256 * 132 * 4
-    delta = (B * H * L * 4 + 255) // 256 * 256
+    stats = B * H * ((L + 63) // 64) * 1024   # LSE log2 e, -Delta and the exponent, 1 KB per query tile
     exps = (4 * n_tiles + 255) // 256 * 256 + 4 * n_tiles
-    # Delta, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents, then the
+    # row statistics, 7 tile arrays (Q fp16, (Rq)^T, dO, dO^T, K fp16, (Rk)^T, V), Q and K tile exponents, then the
     # tail splits (the forward's rule over blocks of 256 keys or queries): the dK/dV passes' fp32 partials
     # of dK~ and dV (64 key blocks x 4 query ranges each), then the dQ pass's (64 query blocks x 4 key ranges)
     kv_part, dq_part = 2 * 64 * 4 * 256 * D * 4, 64 * 4 * 256 * D * 4
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == up(delta + 7 * tiled * 2 + exps) + kv_part + dq_part
-    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == up(delta + 7 * tiled * 2 + exps) + kv_part + dq_part
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 1) == up(stats + 7 * tiled * 2 + exps) + kv_part + dq_part
+    assert lib.wanattn_self_bwd_workspace_bytes(B, L, H, D, 0) == up(stats + 7 * tiled * 2 + exps) + kv_part + dq_part
     # no tail split: the layout ends with the key tile exponents (32 heads: 37 rounds of 256 blocks)
-    d32, t32 = (B * 32 * L * 4 + 255) // 256 * 256, B * 32 * ((L + 63) // 64)
+    t32 = B * 32 * ((L + 63) // 64)
+    d32 = t32 * 1024
     assert lib.wanattn_self_bwd_workspace_bytes(B, L, 32, D, 1) == (
         d32 + 7 * small * 2 + (4 * t32 + 255) // 256 * 256 + 4 * t32)
     assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, 64, 1) == 0
@@ -111,7 +112,8 @@ def test_cross_bwd_workspace_with_query_split(lib):
     assert _q_split(1, 75600, 75600, 40) == 1          # the self-attention backward is not split
     a256 = lambda x: (x + 255) // 256 * 256
     qt, kt = B * H * ((Lq + 63) // 64), B * H * ((Lk + 63) // 64)
-    base = a256(B * H * Lq * 4) + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt
+    # row statistics (1 KB per query tile), 4 query-side and 3 key-side tile arrays, the two exponent arrays
+    base = 1024 * qt + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt
     # then the dK/dV partials of the 7 query ranges (no dK/dV tail split with a query split), then the dQ
     # tail split's (64 query blocks x 4 key ranges)
     assert lib.wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D) == (
@@ -119,7 +121,7 @@ def test_cross_bwd_workspace_with_query_split(lib):
     # no split: the layout ends with the key tile exponents
     qt, kt = 2 * 2 * 2, 2 * 2 * 8                      # 64-token tiles over B x H
     assert lib.wanattn_cross_bwd_workspace_bytes(2, 100, 512, 2, D) == (
-        a256(2 * 2 * 100 * 4) + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt)
+        1024 * qt + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt)
 
 
 def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, L=320, H=2, D=128, g=GRID, r=ROPE, table=P, scale=0.088,
@@ -280,7 +282,7 @@ def test_cross_bwd_validation(lib):
     assert cb(ws_bytes=need - 1) == WS
     # Delta [B, H, Lq] + 4 query-side and 3 key-side tile arrays + the two exponent arrays
     qt, kt = 2 * 2 * 2, 2 * 2 * 8
-    assert need == (2 * 2 * 100 * 4 + 255) // 256 * 256 + 4 * qt * 16384 + 3 * kt * 16384 + 256 + kt * 4
+    assert need == 1024 * qt + 4 * qt * 16384 + 3 * kt * 16384 + 256 + kt * 4
 
 
 def test_fp8_validation(lib):
