@@ -119,8 +119,8 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) tf[kg] = DK_QT + col * 128 + (((2 * kg + half) ^ swz8(col)) << 4);
   const uint32_t sf = DK_ST + 16 * (16 * half + (lane & 15));
-  auto frag = [&](uint32_t off) { return *reinterpret_cast<const bf16x8*>(smem + off); };
-  auto stat4 = [&](uint32_t off) { return *reinterpret_cast<const f32x4*>(smem + off); };
+  auto frag = [&](uint32_t off) __attribute__((always_inline)) { return *reinterpret_cast<const bf16x8*>(smem + off); };
+  auto stat4 = [&](uint32_t off) __attribute__((always_inline)) { return *reinterpret_cast<const f32x4*>(smem + off); };
 
   uint32_t roff[2], toff[2];
 #pragma unroll
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
   const __amdgpu_buffer_rsrc_t dor = tile_rsrc(p.dor + ks.tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t qtr = tile_rsrc(p.qt + ks.tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t str = tile_rsrc(p.qstat + ks.tile0 * QSTAT_FLOATS, (uint32_t)ks.nt * 1024u);
-  auto copy_qd = [&](int slot, int t) {
+  auto copy_qd = [&](int slot, int t) __attribute__((always_inline)) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -141,12 +141,12 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
       buf_dma16(dor, roff[i], soff, smem + DK_QD + 32768 * slot + 16384 + 2048 * wv + 1024 * i);
     }
   };
-  auto copy_qt = [&](int slot, int t) {
+  auto copy_qt = [&](int slot, int t) __attribute__((always_inline)) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) buf_dma16(qtr, toff[i], soff, smem + DK_QT + 16384 * slot + 2048 * wv + 1024 * i);
   };
-  auto copy_stats = [&](int t) {
+  auto copy_stats = [&](int t) __attribute__((always_inline)) {
     if (wv == 0) buf_dma16(str, 16 * lane, (uint32_t)t * 1024u, smem + DK_ST + 1024 * (t & 3));
   };
 
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
     using P1 = std::integral_constant<int, 1>;
     // The copies of interval 2u (tile u = index within the range): Q/dO(u+1) into slot
     // (u+1) & 1, (R q)^T(u) into slot u & 1, statistics(u+1).
-    auto copies = [&](auto parity, int u) {
+    auto copies = [&](auto parity, int u) __attribute__((always_inline)) {
       constexpr int P = decltype(parity)::value;   // u & 1
       if (u + 1 < n) {
         copy_qd(P ^ 1, ks.t0 + u + 1);
@@ -178,14 +178,14 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
     bf16x8 dsf[4];
     // The end of a phase (VMEM: wait for this wave's copies first).  No
     // instruction moves across it: each phase keeps to its own pipe.
-    auto phase_end = [&](bool vmem) {
+    auto phase_end = [&](bool vmem) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       if (vmem) wait_vmem();
       dma_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
     // M(u), parity P = u & 1: dK~ of tile u-1 (GRAD: u > 0), then S and dP of tile u (SDP: u < n).
-    auto m_phase = [&](auto parity, auto grad_tag, auto sdp_tag, int u) {
+    auto m_phase = [&](auto parity, auto grad_tag, auto sdp_tag, int u) __attribute__((always_inline)) {
       constexpr int P = decltype(parity)::value;
       constexpr bool GRAD = decltype(grad_tag)::value;
       constexpr bool SDP = decltype(sdp_tag)::value;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
       phase_end(late);
     };
     // V(u): P = exp2(S g - LSE log2 e), dS = P (dP - Delta), packed to bf16 for the next M.
-    auto v_phase = [&](auto parity, int u) {
+    auto v_phase = [&](auto parity, int u) __attribute__((always_inline)) {
       const int t = ks.t0 + u;
       if (late && u + 1 < n) copies(std::integral_constant<int, decltype(parity)::value ^ 1>{}, u + 1);
       if (!KMASK || ks.wave_live) {
@@ -376,10 +376,23 @@ __global__ __launch_bounds__(256) void bwd_kv_tail_reduce_kernel(BwdParams p, in
 // ---------------------------------------------------------------------------
 // dQ: workgroup owns 256 queries (query tiles 4qb .. 4qb+3); loop over 64-key tiles.
 // ---------------------------------------------------------------------------
+// A wave holds the fp16 Q rows and the dO rows of its 32 queries (B operands
+// of S^T = K Q^T and dP^T = V dO^T; the lane owns query i, so its LSE and
+// Delta are two registers) and accumulates dq~^T += (R k)^T dS^T.  The same
+// ping-pong as the dK pass: M(u) = dq~ of key tile u-1, then S^T and dP^T of
+// tile u; V(u) = P and dS of tile u; waves 4..7 one phase behind.  K/V rows of
+// tile u are read in intervals 2u..2u+1, its (R k)^T in 2u+2..2u+3 (double
+// buffers); in interval 2u every wave copies its share of K/V(u+1) and
+// (R k)^T(u) and waits for them before barrier 2u+1.
+constexpr uint32_t DQ_KV = 0;        // K fp16 row tile at + 32768 * slot, V row tile at + 16384
+constexpr uint32_t DQ_KT = 65536;    // (R k)^T at + 16384 * slot
+constexpr uint32_t DQ_LDS = DQ_KT + 2 * 16384;
+
 // SPLIT: the tail launch (one key range of a query block, fp32 partial of dq~ out).
 template <bool SPLIT>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][3][TILE_ELEMS];   // [buf][K fp16 | (Rk)^T | V]
+__global__ __launch_bounds__(64 * DQ_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+    BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DQ_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -387,6 +400,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool late = wv >= DQ_WAVES / 2;   // waves 4..7: one phase behind
 
   int logical, split = 0;
   if (SPLIT) {
@@ -433,6 +447,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) dq_acc[d] = f32x16{};
 
+  // This lane's LDS byte offsets (slot, 32-key block and matrix are immediates):
+  // row fragments (K, V): row col, chunk 2s + half; (R k)^T: row col, chunk 2kg + half.
+  uint32_t rf[8], tf[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) rf[s] = DQ_KV + col * 256 + (((2 * s + half) ^ swz(col)) << 4);
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) tf[kg] = DQ_KT + col * 128 + (((2 * kg + half) ^ swz8(col)) << 4);
+  auto frag = [&](uint32_t off) __attribute__((always_inline)) { return *reinterpret_cast<const bf16x8*>(smem + off); };
+
   uint32_t roff[2], toff[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -444,80 +467,154 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t ktr = tile_rsrc(p.kt + ktile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t vrr = tile_rsrc(p.vr + ktile0 * TILE_ELEMS, bytes);
   const_i32* kexp = const_ptr(p.kexp + ktile0);   // scalar loads
-
-  auto stage = [&](int buf, int t) {
+  auto copy_kv = [&](int slot, int t) __attribute__((always_inline)) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      buf_dma16(kfr, roff[c], soff, tile_lds_block<DQ_WAVES>(tiles[buf][0], wv, c));
-      buf_dma16(ktr, toff[c], soff, tile_lds_block<DQ_WAVES>(tiles[buf][1], wv, c));
-      buf_dma16(vrr, roff[c], soff, tile_lds_block<DQ_WAVES>(tiles[buf][2], wv, c));
+      buf_dma16(kfr, roff[c], soff, smem + DQ_KV + 32768 * slot + 2048 * wv + 1024 * c);
+      buf_dma16(vrr, roff[c], soff, smem + DQ_KV + 32768 * slot + 16384 + 2048 * wv + 1024 * c);
     }
   };
+  auto copy_kt = [&](int slot, int t) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) buf_dma16(ktr, toff[c], soff, smem + DQ_KT + 16384 * slot + 2048 * wv + 1024 * c);
+  };
 
-  int e_k = 0;
-  if (t1 > t0) {
-    stage(0, t0);
-    e_k = kexp[t0];
-  }
-  wait_vmem();
-  __syncthreads();
-
-  // One 64-key tile; MASK: the last tile when L % 64 != 0 (keys >= L get P = 0).
-  auto key_tile = [&](auto mask_tag, int t, int buf) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint16_t* ks = tiles[buf][0];
-    const uint16_t* kts = tiles[buf][1];
-    const uint16_t* vs = tiles[buf][2];
-    const float g = ldexpf(p.scale_log2, e_q + e_k);
-    bf16x8 dsf[4];
+  // The full key tiles [t0, t0 + n) run as ping-pong phases; a partial last tile (keys past
+  // n_keys get P = 0; only the range that holds it) runs after them in one step.
+  const bool partial_last = t1 > t0 && t1 == nkt && n_keys % TILE_ROWS != 0;
+  const int n = t1 - t0 - (partial_last ? 1 : 0);
+  f32x16 s_acc[2], dp_acc[2];
+  bf16x8 dsf[4];
+  // S^T and dP^T of the tile in K/V slot P; dq~ from (R k)^T slot P (MFMA only).
+  auto sdp = [&](auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+      s_acc[kb] = f32x16{};
+      dp_acc[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        s_acc = mfma32_f16(lds_row_frag(ks, kb * 32 + col, 2 * s + half), qf[s], s_acc);
-        dp_acc = mfma32(lds_row_frag(vs, kb * 32 + col, 2 * s + half), dof[s], dp_acc);
+        s_acc[kb] = mfma32_f16(frag(rf[s] + 32768 * P + 8192 * kb), qf[s], s_acc[kb]);
+        dp_acc[kb] = mfma32(frag(rf[s] + 32768 * P + 16384 + 8192 * kb), dof[s], dp_acc[kb]);
       }
+  };
+  auto grad = [&](auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) dq_acc[d] = mfma32(frag(tf[kg] + 16384 * P + 4096 * d), dsf[kg], dq_acc[d]);
+  };
+  // P = exp2(S g - LSE log2 e), dS = P (dP - Delta) into dsf; MASK: keys past n_keys get P = 0.
+  auto softmax = [&](auto mask_tag, int t, int e_k) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const float g = ldexpf(p.scale_log2, e_q + e_k);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       float dsv[16];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[jj], g, -lse2));
+      for (int j = 0; j < 16; ++j) {
+        float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][j], g, -lse2));
         if (MASK) {
-          const int key = t * TILE_ROWS + kb * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
+          const int key = t * TILE_ROWS + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
           if (key >= n_keys) pe = 0.f;
         }
-        dsv[jj] = pe * (dp_acc[jj] + ndelta);
+        dsv[j] = pe * (dp_acc[kb][j] + ndelta);
       }
       dsf[2 * kb] = pack_acc8(dsv);
       dsf[2 * kb + 1] = pack_acc8(dsv + 8);
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
-        dq_acc[d] = mfma32(lds_vt_frag(kts, d * 32 + col, kg, half), dsf[kg], dq_acc[d]);
-      }
+      __builtin_amdgcn_sched_barrier(0);   // one 32-key half at a time (registers)
     }
   };
-
-  // Full tiles in the loop; a partial last tile is peeled off after it (only by the range that holds it:
-  // an empty range, t0 == t1 == nkt, has n_full == t1).
-  const int n_full = max(t0, min(n_keys / TILE_ROWS, t1));
-  for (int t = t0; t < n_full; ++t) {
-    const int buf = (t - t0) & 1;
-    const bool has_next = t + 1 < t1;
-    int e_k_next = 0;
-    if (has_next) {
-      stage(buf ^ 1, t + 1);
-      e_k_next = kexp[t + 1];
-    }
-    key_tile(std::false_type{}, t, buf);
-    if (has_next) wait_vmem();
+  if (n > 0) {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // The copies of interval 2u: K/V(u+1) into slot (u+1) & 1, (R k)^T(u) into slot u & 1.
+    auto copies = [&](auto parity, int u) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;   // u & 1
+      if (u + 1 < n) copy_kv(P ^ 1, t0 + u + 1);
+      copy_kt(P, t0 + u);
+    };
+    copy_kv(0, t0);
+    int e_k = kexp[t0];   // exponent of the tile whose softmax comes next
+    wait_vmem();
     __syncthreads();
-    e_k = e_k_next;
+    if (late) {
+      copies(P0{}, 0);   // interval 0: the late waves' "V(-1)"
+      dma_barrier();     // the early waves run M(0) meanwhile
+    }
+    auto phase_end = [&](bool vmem) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (vmem) wait_vmem();
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // M(u), parity P = u & 1: dq~ of tile u-1 (GRAD: u > 0), then S^T and dP^T of tile u (SDP: u < n).
+    auto m_phase = [&](auto parity, auto grad_tag, auto sdp_tag, int u) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;
+      constexpr bool GRAD = decltype(grad_tag)::value;
+      constexpr bool SDP = decltype(sdp_tag)::value;
+      if (SDP && !late) copies(parity, u);
+      if (GRAD) grad(std::integral_constant<int, P ^ 1>{});
+      if (SDP) sdp(parity);
+      // Keep four fragment reads in flight ahead of the MFMAs.
+      constexpr int n_mfma = (GRAD ? 16 : 0) + (SDP ? 32 : 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < n_mfma - 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      phase_end(late);
+    };
+    // V(u): the softmax of tile u; the late waves copy for interval 2u+2 first.
+    auto v_phase = [&](auto parity, int u) __attribute__((always_inline)) {
+      const int t = t0 + u;
+      if (late && u + 1 < n) copies(std::integral_constant<int, decltype(parity)::value ^ 1>{}, u + 1);
+      const int e_t = e_k;
+      if (u + 1 < n) e_k = kexp[t + 1];   // scalar load, waited for at the barrier
+      softmax(std::false_type{}, t, e_t);
+      // dS is complete here: the code sinking passes must not move its
+      // arithmetic past the barrier into the next products phase.
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pin_vgprs(dsf[k]);
+      phase_end(!late);
+    };
+    m_phase(P0{}, std::false_type{}, std::true_type{}, 0);
+    v_phase(P0{}, 0);
+    int u = 1;
+    for (; u + 1 < n; u += 2) {
+      m_phase(P1{}, std::true_type{}, std::true_type{}, u);
+      v_phase(P1{}, u);
+      m_phase(P0{}, std::true_type{}, std::true_type{}, u + 1);
+      v_phase(P0{}, u + 1);
+    }
+    if (u < n) {
+      m_phase(P1{}, std::true_type{}, std::true_type{}, u);
+      v_phase(P1{}, u);
+    }
+    // M(n): the last full tile's dq~ product
+    if (n & 1) m_phase(P1{}, std::true_type{}, std::false_type{}, n);
+    else m_phase(P0{}, std::true_type{}, std::false_type{}, n);
+    if (!late) dma_barrier();   // matches the late waves' barrier before their M(0)
   }
-  if (n_full < t1) key_tile(std::true_type{}, n_full, (n_full - t0) & 1);
+  if (partial_last) {
+    // Every wave has left the slots (the last barrier above, or none used).
+    const int t = t1 - 1;
+    copy_kv(0, t);
+    copy_kt(0, t);
+    wait_vmem();
+    __syncthreads();
+    sdp(std::integral_constant<int, 0>{});
+    softmax(std::true_type{}, t, kexp[t]);
+    grad(std::integral_constant<int, 0>{});
+  }
 
   if (SPLIT) {
     // Partial dq~ of this key range (unscaled, unrotated): rows of 128 fp32.
