@@ -74,17 +74,6 @@ constexpr uint32_t DK_ST = 98304;    // statistics at + 1024 * (tile & 3)
 constexpr uint32_t DK_LDS = DK_ST + 4 * 1024;
 static_assert(QSTAT_FLOATS * 4 == 1024, "one 1 KB copy per statistics tile");
 
-// out[j] = x of lane j of this lane's 16-lane row (DPP row_newbcast:j).
-template <int... J>
-__device__ __forceinline__ void row_bcast16_impl(float x, float* out, std::integer_sequence<int, J...>) {
-  ((out[J] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf,
-                                                                   0xf, false))),
-   ...);
-}
-__device__ __forceinline__ void row_bcast16(float x, float (&out)[16]) {
-  row_bcast16_impl(x, out, std::make_integer_sequence<int, 16>{});
-}
-
 template <bool KMASK, bool TAIL>
 __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dk_kernel(
     BwdParams p) {

@@ -5,6 +5,7 @@
 // while the register-bound dK and dQ passes spill or slow down under it.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "bwd_common.h"
 
@@ -15,19 +16,23 @@ namespace {
 using namespace bwd;
 
 // dV_j = sum_i P_ij dO_i.  Workgroup = 256 keys (8 waves, one workgroup per
-// CU: each query tile crosses from L2 once per CU, not once per 128 keys);
-// query tiles staged as Q fp16 rows and dO^T.  S = Q K^T from the
-// wave's K rows in registers, dV^T += dO^T P with P from the accumulators.
+// CU, two waves per SIMD); query tiles staged as Q fp16 rows, dO^T and the
+// row statistics.  S = Q K^T from the wave's K rows in registers, dV^T +=
+// dO^T P with P from the accumulators.  The same ping-pong as the dK pass
+// (attn_bwd.hip): M(u) = dV of query tile u-1, then S of tile u; V(u) = P of
+// tile u, its LSE reaching each lane by DPP row broadcast from one 16-byte
+// read of the tile statistics; waves 4..7 one phase behind; Q(u+1), dO^T(u)
+// and the statistics of u+1 copied in interval 2u and waited for before
+// barrier 2u+1.
+constexpr uint32_t DV_Q = 0;         // Q row tile at + 16384 * slot
+constexpr uint32_t DV_DOT = 32768;   // dO^T at + 16384 * slot
+constexpr uint32_t DV_ST = 65536;    // statistics at + 1024 * (tile & 3)
+constexpr uint32_t DV_LDS = DV_ST + 4 * 1024;
+
 template <bool KMASK, bool TAIL>
-__global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
-  // Double-buffered tiles as separate objects, named statically in the
-  // two-way unrolled loop (LDS reads do not wait for copies in flight).
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse2_s0[TILE_ROWS];   // LSE * log2 e (+inf: no row)
-  __shared__ __attribute__((aligned(16))) float lse2_s1[TILE_ROWS];
+__global__ __launch_bounds__(64 * DV_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dv_kernel(
+    BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DV_LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -35,6 +40,7 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool late = wv >= DV_WAVES / 2;   // waves 4..7: one phase behind
   const KeySide ks = key_side<DV_WAVES, KMASK, TAIL>(p, wv, col);
 
   bf16x8 kf[8];   // K fp16 (bit patterns): B operand of S
@@ -45,113 +51,155 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) void bwd_dv_kernel(BwdParams p) {
   f32x16 dv_acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) dv_acc[d] = f32x16{};
-  const float* lse_row = p.lse + ((int64_t)ks.b * p.H + ks.h) * p.Lq;
 
-  constexpr int NCP = 16 / DV_WAVES;   // 1 KB copies per wave and tile
-  uint32_t roff[NCP], toff[NCP];
+  // This lane's LDS byte offsets (slot, row block and matrix are immediates).
+  uint32_t rf[8], tf[4];
 #pragma unroll
-  for (int i = 0; i < NCP; ++i) {
+  for (int s = 0; s < 8; ++s) rf[s] = DV_Q + col * 256 + (((2 * s + half) ^ swz(col)) << 4);
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) tf[kg] = DV_DOT + col * 128 + (((2 * kg + half) ^ swz8(col)) << 4);
+  const uint32_t sf = DV_ST + 16 * (16 * half + (lane & 15));
+  auto frag = [&](uint32_t off) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(smem + off);
+  };
+
+  uint32_t roff[2], toff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
     roff[i] = rowtile_lane_off<DV_WAVES>(wv, i, lane);
     toff[i] = ttile_lane_off<DV_WAVES>(wv, i, lane);
   }
   const uint32_t bytes = (uint32_t)ks.nt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
   const __amdgpu_buffer_rsrc_t qfr = tile_rsrc(p.qf + ks.tile0 * TILE_ELEMS, bytes);
   const __amdgpu_buffer_rsrc_t dotr = tile_rsrc(p.dot + ks.tile0 * TILE_ELEMS, bytes);
-  const_i32* qexp = const_ptr(p.qexp + ks.tile0);   // scalar loads
-
-  struct Buf {
-    uint16_t* q;
-    uint16_t* dOt;
-    float* lse2;
-  };
-  const Buf buf0{q_lds0, dot_lds0, lse2_s0};
-  const Buf buf1{q_lds1, dot_lds1, lse2_s1};
-  auto stage = [&](const Buf& dst, int t) {
+  const __amdgpu_buffer_rsrc_t str = tile_rsrc(p.qstat + ks.tile0 * QSTAT_FLOATS, (uint32_t)ks.nt * 1024u);
+  auto copy_q = [&](int slot, int t) __attribute__((always_inline)) {
     const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
 #pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      buf_dma16(qfr, roff[i], soff, tile_lds_block<DV_WAVES>(dst.q, wv, i));
-      buf_dma16(dotr, toff[i], soff, tile_lds_block<DV_WAVES>(dst.dOt, wv, i));
-    }
+    for (int i = 0; i < 2; ++i) buf_dma16(qfr, roff[i], soff, smem + DV_Q + 16384 * slot + 2048 * wv + 1024 * i);
   };
-  // LSE of query tile t: threads 0..63, into a register, published to LDS
-  // once loaded (rows past Lq, and rows with no valid key, get +inf: P = 0).
-  auto load_stats = [&](int t) {
-    float x = -INFINITY;
-    if (tid < TILE_ROWS) {
-      const int i = t * TILE_ROWS + tid;
-      if (i < p.Lq) x = lse_row[i];
-    }
-    return x;
+  auto copy_dot = [&](int slot, int t) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)t * (TILE_ELEMS * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buf_dma16(dotr, toff[i], soff, smem + DV_DOT + 16384 * slot + 2048 * wv + 1024 * i);
   };
-  auto store_stats = [&](const Buf& dst, float x) {
-    if (tid < TILE_ROWS) dst.lse2[tid] = (x > -INFINITY) ? x * LOG2E : INFINITY;
+  auto copy_stats = [&](int t) __attribute__((always_inline)) {
+    if (wv == 0) buf_dma16(str, 16 * lane, (uint32_t)t * 1024u, smem + DV_ST + 1024 * (t & 3));
   };
 
   // A query split can be empty (rounding of the split size): it writes zero partials.
-  if (ks.t0 < ks.t1) {
-    int e_q;
-    {
-      const float st = load_stats(ks.t0);
-      stage(buf0, ks.t0);
-      e_q = qexp[ks.t0];
-      wait_vmem();
-      store_stats(buf0, st);
-    }
-    __syncthreads();
-
-    auto iteration = [&](auto parity, int t) {
-      constexpr int P = decltype(parity)::value;
-      const Buf& cur = P ? buf1 : buf0;
-      const Buf& nxt = P ? buf0 : buf1;
-      const bool has_next = t + 1 < ks.t1;
-      int e_q_next = 0;
-      float st = 0.f;
-      if (has_next) {
-        st = load_stats(t + 1);
-        stage(nxt, t + 1);
-        e_q_next = qexp[t + 1];
+  const int n = ks.t1 - ks.t0;
+  if (n > 0) {
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // The copies of interval 2u: Q(u+1) into slot (u+1) & 1, dO^T(u) into slot u & 1, statistics(u+1).
+    auto copies = [&](auto parity, int u) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;   // u & 1
+      if (u + 1 < n) {
+        copy_q(P ^ 1, ks.t0 + u + 1);
+        copy_stats(ks.t0 + u + 1);
       }
-      const float g = ldexpf(p.scale_log2, e_q + e_k);
-      bf16x8 pf[4];
-  #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s_acc = f32x16{};
-  #pragma unroll
-        for (int s = 0; s < 8; ++s) s_acc = mfma32_f16(lds_row_frag(cur.q, qb * 32 + col, 2 * s + half), kf[s], s_acc);
-        float pv[16];
-  #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // rows qb*32 + 8m + 4*half + (0..3) of this tile: the accumulator's row order
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.lse2 + qb * 32 + 8 * m + 4 * half);
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[4 * m + e], g, -l4[e]));
-            if (KMASK && !ks.key_live) pe = 0.f;
-            pv[4 * m + e] = pe;
-          }
-        }
-        pf[2 * qb] = pack_acc8(pv);
-        pf[2 * qb + 1] = pack_acc8(pv + 8);
-      }
-  #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-  #pragma unroll
-        for (int qg = 0; qg < 4; ++qg) dv_acc[d] = mfma32(lds_vt_frag(cur.dOt, d * 32 + col, qg, half), pf[qg], dv_acc[d]);
-      }
-      if (has_next) {
-        wait_vmem();
-        store_stats(nxt, st);
-      }
-      __syncthreads();
-      e_q = e_q_next;
+      copy_dot(P, ks.t0 + u);
     };
-    int t = ks.t0;
-    for (; t + 1 < ks.t1; t += 2) {
-      iteration(std::integral_constant<int, 0>{}, t);
-      iteration(std::integral_constant<int, 1>{}, t + 1);
+    copy_q(0, ks.t0);
+    copy_stats(ks.t0);
+    wait_vmem();
+    __syncthreads();
+    if (late) {
+      copies(P0{}, 0);   // interval 0: the late waves' "V(-1)"
+      dma_barrier();     // the early waves run M(0) meanwhile
     }
-    if (t < ks.t1) iteration(std::integral_constant<int, 0>{}, t);
+
+    f32x16 s_acc[2];
+    bf16x8 pf[4];
+    auto phase_end = [&](bool vmem) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (vmem) wait_vmem();
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // M(u), parity P = u & 1: dV of tile u-1 (GRAD: u > 0), then S of tile u (SDP: u < n).
+    auto m_phase = [&](auto parity, auto grad_tag, auto sdp_tag, int u) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;
+      constexpr bool GRAD = decltype(grad_tag)::value;
+      constexpr bool SDP = decltype(sdp_tag)::value;
+      if (SDP && !late) copies(parity, u);
+      if (!KMASK || ks.wave_live) {
+        if (GRAD) {
+#pragma unroll
+          for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              dv_acc[d] = mfma32(frag(tf[kg] + 16384 * (P ^ 1) + 4096 * d), pf[kg], dv_acc[d]);
+        }
+        if (SDP) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) s_acc[qb] = f32x16{};
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              s_acc[qb] = mfma32_f16(frag(rf[s] + 16384 * P + 8192 * qb), kf[s], s_acc[qb]);
+        }
+        // Keep six fragment reads in flight ahead of the MFMAs (registers allow it here).
+        constexpr int n_mfma = (GRAD ? 16 : 0) + (SDP ? 16 : 0);
+        constexpr int AHEAD = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+        for (int k = 0; k < n_mfma - AHEAD; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+      }
+      phase_end(late);
+    };
+    // V(u): P = exp2(S g - LSE log2 e), packed to bf16 for the next M.
+    auto v_phase = [&](auto parity, int u) __attribute__((always_inline)) {
+      const int t = ks.t0 + u;
+      if (late && u + 1 < n) copies(std::integral_constant<int, decltype(parity)::value ^ 1>{}, u + 1);
+      if (!KMASK || ks.wave_live) {
+        // {LSE log2 e, -Delta} x 2 row blocks per entry, the tile exponent after the entries
+        const f32x4 st = *reinterpret_cast<const f32x4*>(smem + sf + 1024 * (t & 3));
+        const int e_q = *reinterpret_cast<const int*>(smem + DV_ST + 1024 * (t & 3) + 512);
+        const float g = ldexpf(p.scale_log2, e_q + e_k);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float l2[16], pv[16];
+          row_bcast16(qb ? st[2] : st[0], l2);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[qb][j], g, -l2[j]));
+            if (KMASK && !ks.key_live) pe = 0.f;
+            pv[j] = pe;
+          }
+          pf[2 * qb] = pack_acc8(pv);
+          pf[2 * qb + 1] = pack_acc8(pv + 8);
+        }
+        // P is complete here: the code sinking passes must not move its
+        // arithmetic past the barrier into the next products phase.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin_vgprs(pf[i]);
+      }
+      phase_end(!late);
+    };
+    m_phase(P0{}, std::false_type{}, std::true_type{}, 0);
+    v_phase(P0{}, 0);
+    int u = 1;
+    for (; u + 1 < n; u += 2) {
+      m_phase(P1{}, std::true_type{}, std::true_type{}, u);
+      v_phase(P1{}, u);
+      m_phase(P0{}, std::true_type{}, std::true_type{}, u + 1);
+      v_phase(P0{}, u + 1);
+    }
+    if (u < n) {
+      m_phase(P1{}, std::true_type{}, std::true_type{}, u);
+      v_phase(P1{}, u);
+    }
+    // M(n): the last tile's dV product
+    if (n & 1) m_phase(P1{}, std::true_type{}, std::false_type{}, n);
+    else m_phase(P0{}, std::true_type{}, std::false_type{}, n);
+    if (!late) dma_barrier();   // matches the late waves' barrier before their M(0)
   }
 
   if (TAIL) {

@@ -4,6 +4,8 @@
 // fragments of a row tile, and the key-side setup of the dK and dV passes.
 #pragma once
 
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -27,6 +29,17 @@ __device__ __forceinline__ void store_grad4(uint16_t* row_ptr, const RopeDev& ro
   w[0] = pack_bf16(g0, g1);
   w[1] = pack_bf16(g2, g3);
   *reinterpret_cast<u32x2*>(row_ptr + d0) = w;
+}
+
+// out[j] = x of lane j of this lane's 16-lane row (DPP row_newbcast:j).
+template <int... J>
+__device__ __forceinline__ void row_bcast16_impl(float x, float* out, std::integer_sequence<int, J...>) {
+  ((out[J] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf,
+                                                                   0xf, false))),
+   ...);
+}
+__device__ __forceinline__ void row_bcast16(float x, float (&out)[16]) {
+  row_bcast16_impl(x, out, std::make_integer_sequence<int, 16>{});
 }
 
 // Row `r` of a row tile in global memory as the 8 register fragments of the
