@@ -69,6 +69,8 @@ def parse():
                     help="skip the per-workload forward timings and the MFMA loop (profiling runs of the step)")
     ap.add_argument("--configs-only", action="store_true",
                     help="only the per-workload forward timings and the MFMA loop (profiling runs of those)")
+    ap.add_argument("--cross-only", action="store_true",
+                    help="only the text cross-attention forward and backward at the 720p text shape (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain device copy of known size (for scaling HBM counters)")
     return ap.parse_args()
@@ -232,6 +234,29 @@ def bench_configs(wa, torch, synth, dev, rope, peak_meas, c4_ms):
     return {k: out[k] for k in ("C1", "C2", "C3", "C4", "C5") if k in out}
 
 
+def bench_cross(wa, torch, dev, g, with_fwd=False):
+    """Text cross-attention at the step's shape: 75,600 video tokens over 512 text tokens (336 valid), 40 heads;
+    the backward (and with_fwd: the forward) timed on its own."""
+    out = {}
+    L, H, Lt = 75600, 40, 512
+    q, do = (torch.randn((1, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    tk, tv = (torch.randn((1, Lt, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    kl = torch.tensor([336], dtype=torch.int32, device=dev)
+    o, lse = torch.empty_like(q), torch.empty((1, H, L), dtype=torch.float32, device=dev)
+    wsf = torch.empty(wa.cross_fwd_workspace_bytes(1, Lt, H), dtype=torch.uint8, device=dev)
+    ms = _time(lambda: wa.cross_fwd(q, tk, tv, kl, out=o, lse=lse, workspace=wsf), reps=20)
+    if with_fwd:
+        out["cross_fwd"] = {"workload": "720p video tokens (75,600) over 512 text tokens (336 valid), 40 heads",
+                            "ms": round(ms, 4), "tflops": round(4.0 * H * L * 336 * 128 / (ms * 1e-3) / 1e12, 1)}
+    ws = torch.empty(wa.cross_bwd_workspace_bytes(1, L, Lt, H), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(tk), torch.empty_like(tv)
+    ms = _time(lambda: wa.cross_bwd(q, tk, tv, kl, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv))
+    flop = 8.0 * H * L * 336 * 128
+    out["cross_bwd"] = {"workload": "720p video tokens (75,600) over 512 text tokens (336 valid), 40 heads",
+                        "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    return out
+
+
 def bench_next_rows(wa, torch, synth, dev, rope):
     """The rows beyond the step, each on its own realistic shape (timed after the step, not in it):
     - one Ring hop of Ulysses-8 x Ring-2 context parallelism at 256K tokens (grid 64x64x64): a
@@ -263,19 +288,7 @@ def bench_next_rows(wa, torch, synth, dev, rope):
     out["lse_merge"] = {"workload": "2 partials [1, 131072, 5, 128] bf16 + LSE", "ms": round(ms, 4),
                         "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
     del q, k, v, o1, o2, om, ws
-    # text cross-attention backward at the step's shape: 75,600 video tokens over 512 text tokens (336 valid)
-    L, H, Lt = 75600, 40, 512
-    q, do = (torch.randn((1, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
-    tk, tv = (torch.randn((1, Lt, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
-    kl = torch.tensor([336], dtype=torch.int32, device=dev)
-    o, lse = wa.cross_fwd(q, tk, tv, kl)
-    ws = torch.empty(wa.cross_bwd_workspace_bytes(1, L, Lt, H), dtype=torch.uint8, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(tk), torch.empty_like(tv)
-    ms = _time(lambda: wa.cross_bwd(q, tk, tv, kl, o, lse, do, workspace=ws, dq=dq, dk=dk, dv=dv))
-    flop = 8.0 * H * L * 336 * 128
-    out["cross_bwd"] = {"workload": "720p video tokens (75,600) over 512 text tokens (336 valid), 40 heads",
-                        "ms": round(ms, 3), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
-    del q, do, tk, tv, o, ws, dq, dk, dv
+    out["cross_bwd"] = bench_cross(wa, torch, dev, g)["cross_bwd"]
     # FP8 (e4m3) forward on the headline workload: 720p, 40 heads, 3D RoPE
     L, H = 75600, 40
     q, k, v = (torch.randn((1, L, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
@@ -334,6 +347,10 @@ def main():
         return
 
     rope = wa.RopeConfig(48, 40, 40, 10000.0)
+    if args.cross_only:
+        print(json.dumps(bench_cross(wa, torch, dev, torch.Generator(device=dev).manual_seed(7), with_fwd=True)),
+              flush=True)
+        return
     if args.configs_only:
         peak = measure_mfma_peak(wa)
         print(json.dumps({"mfma_peak_measured": peak,
