@@ -74,17 +74,24 @@ static_assert(PP_BR == FWD_ROWS, "the tail split and its workspace assume 256-ro
 // VARLEN: the main launch with variable lengths, where a workgroup whose query
 // tile lies wholly past its item's length leaves at once (an instantiation of
 // its own, so the fixed-length code is unaffected).
-template <bool POS_SCALE, bool F16, bool SPLIT, bool VARLEN>
-// Two waves per SIMD by design (one workgroup per CU); without the explicit
-// target the compiler aims for four (the LDS would allow two workgroups) and
-// schedules for register pressure instead of latency.
-__global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(
+// NW: waves per workgroup.  8: the ping-pong pairs above, one workgroup per
+// CU.  4 (short key sequences such as the text context, 128 query rows): no
+// phase offset inside the workgroup; two workgroups share each CU, so one
+// loads its queries or stores its output while the other computes.
+template <bool POS_SCALE, bool F16, bool SPLIT, bool VARLEN, int NW = PP_WAVES>
+// Two waves per SIMD by design; without the explicit target the compiler aims
+// for four (the LDS would allow more) and schedules for register pressure
+// instead of latency.
+__global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(
     FwdParams p) {
+  static_assert(NW == 8 || NW == 4, "8 ping-pong waves or 4 plain ones");
+  constexpr int BR = 32 * NW;          // query rows per workgroup
+  constexpr int NCP = 16 / NW;         // 1 KB copies per wave of every K and V tile
   __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t k_lds1[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[TILE_ELEMS];
-  __shared__ float qmax_s[PP_WAVES];
+  __shared__ float qmax_s[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   const int half = lane >> 5;
   const int col = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const bool late = wv >= PP_WAVES / 2;   // waves 4..7: one phase behind
+  const bool late = NW == 8 && wv >= NW / 2;   // waves 4..7: one phase behind
 
   int logical, split = 0;
   if (SPLIT) {
@@ -113,11 +120,11 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   const int nkt = (p.Lk + FWD_BC - 1) / FWD_BC;
   const int64_t tile0 = (int64_t)(b * p.H + h) * nkt;
 
-  const int i = qt * PP_BR + wave * 32 + col;
+  const int i = qt * BR + wave * 32 + col;
   int n_q = p.Lq;
   if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
   const bool row_ok = i < n_q;
-  if (VARLEN && qt * PP_BR >= n_q) return;   // before the first barrier; nothing to compute or store
+  if (VARLEN && qt * BR >= n_q) return;   // before the first barrier; nothing to compute or store
   bf16x8 qf[8];
   float g_q = p.scale_log2;
   {
@@ -185,25 +192,25 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   }
 
   if (t_end > t_begin) {
-    // Each wave copies 1/8 of every K and V tile (2 x 1 KB each).
-    uint32_t koff[2], voff[2];
+    // Each wave copies 1/NW of every K and V tile (NCP x 1 KB each).
+    uint32_t koff[NCP], voff[NCP];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      koff[c] = rowtile_lane_off<PP_WAVES>(wv, c, lane);
-      voff[c] = ttile_lane_off<PP_WAVES>(wv, c, lane);
+    for (int c = 0; c < NCP; ++c) {
+      koff[c] = rowtile_lane_off<NW>(wv, c, lane);
+      voff[c] = ttile_lane_off<NW>(wv, c, lane);
     }
     const uint32_t bytes = (uint32_t)nkt * (TILE_ELEMS * 2);   // < 2^32, checked by the launcher
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(p.kt + tile0 * TILE_ELEMS, bytes);
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(p.vt + tile0 * TILE_ELEMS, bytes);
     auto stage_k = [&](uint16_t* dst, int t) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        buf_dma16(krs, koff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<PP_WAVES>(dst, wv, c));
+      for (int c = 0; c < NCP; ++c)
+        buf_dma16(krs, koff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<NW>(dst, wv, c));
     };
     auto stage_v = [&](uint16_t* dst, int t) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        buf_dma16(vrs, voff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<PP_WAVES>(dst, wv, c));
+      for (int c = 0; c < NCP; ++c)
+        buf_dma16(vrs, voff[c], (uint32_t)t * (TILE_ELEMS * 2), tile_lds_block<NW>(dst, wv, c));
     };
 
     f32x16 s_acc[2];
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(64 * PP_WAVES, 1) __attribute__((amdgpu_waves_per_e
   if (SPLIT) {
     // Partial of this key range: O unnormalized, the running max m (log2
     // units; -inf for an empty range) and l = sum of P against it.
-    float* dst = p.part + ((int64_t)blockIdx.x * PP_BR + wave * 32 + col) * FWD_PART_FLOATS;
+    float* dst = p.part + ((int64_t)blockIdx.x * BR + wave * 32 + col) * FWD_PART_FLOATS;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -464,6 +471,18 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
   const bool f16 = p.rope.table != nullptr;   // fp16 scores against the fp16 key tiles
   if (f16 && p.kexp == nullptr) return hipErrorInvalidValue;
   FwdParams r = p;
+  // Short key sequences (at most 8 tiles: the text context), without a tail split or variable query
+  // lengths: 4-wave workgroups of 128 query rows, two per CU.
+  const bool short_keys = p.part == nullptr && p.q_lens == nullptr && !f16 && (p.Lk + FWD_BC - 1) / FWD_BC <= 8;
+  if (short_keys) {
+    r.n_qtiles = (p.Lq + 127) / 128;
+    const int64_t n4 = (int64_t)r.n_qtiles * p.H * p.B;
+    if (n4 <= 0 || n4 > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)n4);
+    if (p.scale_log2 > 0.f) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, false, 4>), grid, dim3(256), 0, stream, r);
+    else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, false, 4>), grid, dim3(256), 0, stream, r);
+    return hipGetLastError();
+  }
   r.n_qtiles = (p.Lq + PP_BR - 1) / PP_BR;
   const int64_t n = (int64_t)r.n_qtiles * p.H * p.B;
   if (n <= 0 || n > 0x7fffffff) return hipErrorInvalidValue;
