@@ -108,9 +108,23 @@ int bwd_q_split(int B, int Lq, int Lk, int H) {
   const int64_t key_blocks = ((int64_t)Lk + 255) / 256 * H * B;   // dK workgroups without a split
   if (key_blocks <= 0 || key_blocks >= 256) return 1;
   const int64_t nt = ((int64_t)Lq + 63) / 64;
-  int64_t s = (512 + key_blocks - 1) / key_blocks;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, nt / 8));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 32));
+  // At least two rounds of 256 workgroups, at most 32 ranges of >= 8 query tiles each; among those, the
+  // split whose last round is fullest (the smallest on a tie): a third round of 48 workgroups would leave
+  // four fifths of the chip idle for a third of the pass.
+  const int64_t lo = (512 + key_blocks - 1) / key_blocks;
+  const int64_t hi = std::max<int64_t>(1, std::min<int64_t>(32, nt / 8));
+  if (lo >= hi) return (int)hi;
+  int64_t best = lo;
+  double best_fill = 0.0;
+  for (int64_t s = lo; s <= hi; ++s) {
+    const int64_t n = key_blocks * s;
+    const double fill = (double)n / (double)(256 * ((n + 255) / 256));
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = s;
+    }
+  }
+  return (int)best;
 }
 
 BwdWsLayout bwd_ws_layout(int B, int Lq, int Lk, int H, int D) {

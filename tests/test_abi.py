@@ -97,27 +97,30 @@ def test_workspace_sizes(lib):
 
 
 def _q_split(B, Lq, Lk, H):
-    """Query-range split of the dK/dV passes: none while the key blocks of 256 give >= 256 workgroups."""
+    """Query-range split of the dK/dV passes: none while the key blocks of 256 give >= 256 workgroups; else at
+    least two rounds of 256 workgroups, at most 32 ranges of >= 8 query tiles, the fullest last round."""
     blocks = (Lk + 255) // 256 * H * B
     if blocks >= 256:
         return 1
-    s = -(-512 // blocks)
-    s = min(s, max(1, ((Lq + 63) // 64) // 8))
-    return max(1, min(s, 32))
+    lo, hi = -(-512 // blocks), max(1, min(32, ((Lq + 63) // 64) // 8))
+    if lo >= hi:
+        return hi
+    fill = lambda s: blocks * s / (256 * -(-(blocks * s) // 256))
+    return max(range(lo, hi + 1), key=lambda s: (fill(s), -s))
 
 
 def test_cross_bwd_workspace_with_query_split(lib):
     B, Lq, Lk, H, D = 1, 75600, 512, 40, 128          # 720p video tokens over 512 text tokens
-    assert _q_split(B, Lq, Lk, H) == 7
+    assert _q_split(B, Lq, Lk, H) == 16               # 80 key blocks x 16 ranges: 5 full rounds
     assert _q_split(1, 75600, 75600, 40) == 1          # the self-attention backward is not split
     a256 = lambda x: (x + 255) // 256 * 256
     qt, kt = B * H * ((Lq + 63) // 64), B * H * ((Lk + 63) // 64)
     # row statistics (1 KB per query tile), 4 query-side and 3 key-side tile arrays, the two exponent arrays
     base = 1024 * qt + 4 * a256(qt * 64 * D * 2) + 3 * a256(kt * 64 * D * 2) + a256(4 * qt) + 4 * kt
-    # then the dK/dV partials of the 7 query ranges (no dK/dV tail split with a query split), then the dQ
+    # then the dK/dV partials of the 16 query ranges (no dK/dV tail split with a query split), then the dQ
     # tail split's (64 query blocks x 4 key ranges)
     assert lib.wanattn_cross_bwd_workspace_bytes(B, Lq, Lk, H, D) == (
-        a256(a256(base) + 2 * 7 * B * H * Lk * D * 4) + 64 * 4 * 256 * D * 4)
+        a256(a256(base) + 2 * 16 * B * H * Lk * D * 4) + 64 * 4 * 256 * D * 4)
     # no split: the layout ends with the key tile exponents
     qt, kt = 2 * 2 * 2, 2 * 2 * 8                      # 64-token tiles over B x H
     assert lib.wanattn_cross_bwd_workspace_bytes(2, 100, 512, 2, D) == (

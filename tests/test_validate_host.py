@@ -121,8 +121,8 @@ def test_split_rules(h):
     h.h_fwd_tail_split(1, 2048, 130, out)
     assert list(out) == [1040, 1024, 16, 8]                         # S capped at 8
     assert h.h_bwd_q_split(1, L720, L720, H720) == 1                # 11,840 key blocks fill the chip
-    assert h.h_bwd_q_split(1, L720, 512, H720) == 7                 # 80 key blocks: ~512 workgroups
-    assert h.h_bwd_q_split(2, 32760, 512, 12) == 11
+    assert h.h_bwd_q_split(1, L720, 512, H720) == 16                # 80 key blocks: 1,280 workgroups, 5 full rounds
+    assert h.h_bwd_q_split(2, 32760, 512, 12) == 16                 # 48 key blocks: 768 workgroups, 3 full rounds
     assert h.h_bwd_q_split(1, 512, 512, 1) == 1                     # each split needs >= 8 query tiles
 
 
