@@ -276,11 +276,10 @@ def test_cross_all_valid_and_empty():
     assert np.all(o2[1] == 0.0) and np.all(np.isneginf(lse2[1]))
 
 
-def test_cross_persistent_stream():
-    """The persistent kernel walks each workgroup's query tiles as one stream of (query tile, key tile)
-    pairs: 4 items x 3 heads x 125 query tiles (15,950 rows: the last tile holds 78) give 1,500 tiles over
-    512 workgroups, so streams cross query tiles, heads and items, including an item
-    with no valid key (k_len 0), one with a single partial key tile (k_len 1) and a masked last tile."""
+def test_cross_many_items_and_heads():
+    """One launch over 4 items x 3 heads x 125 query tiles of 128 rows (15,950 rows: the last tile holds 78;
+    the short-key path of 4-wave workgroups): items with 77 valid keys (a masked last key tile), one (a single
+    partial key tile), none, and all 200, NaN in the padded keys and values."""
     B, Lq, Lk, H = 4, 15_950, 200, 3
     qb = synth.random_bf16(331, (B, Lq, H, 128))
     kb = synth.random_bf16(332, (B, Lk, H, 128))
