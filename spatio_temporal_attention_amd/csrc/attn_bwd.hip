@@ -181,6 +181,13 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
       const int t = ks.t0 + u;
       if (SDP && !late) copies(parity, u);
       if (!KMASK || ks.wave_live) {
+        // -Delta of the accumulator's rows: {LSE log2 e, -Delta} x 2 blocks per entry; read first, so that
+        // its wait does not drain the fragment reads queued behind it
+        f32x4 st = f32x4{};
+        if (SDP) {
+          st = stat4(sf + 1024 * (t & 3));
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (GRAD) {
 #pragma unroll
           for (int kg = 0; kg < 4; ++kg)
@@ -189,8 +196,6 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
               dk_acc[d] = mfma32(frag(tf[kg] + 16384 * (P ^ 1) + 4096 * d), dsf[kg], dk_acc[d]);
         }
         if (SDP) {
-          // -Delta of the accumulator's rows: {LSE log2 e, -Delta} x 2 blocks per entry
-          const f32x4 st = stat4(sf + 1024 * (t & 3));
           float nd[2][16];
           row_bcast16(st[1], nd[0]);
           row_bcast16(st[3], nd[1]);

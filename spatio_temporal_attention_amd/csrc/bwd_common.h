@@ -34,8 +34,9 @@ __device__ __forceinline__ void store_grad4(uint16_t* row_ptr, const RopeDev& ro
 // out[j] = x of lane j of this lane's 16-lane row (DPP row_newbcast:j).
 template <int... J>
 __device__ __forceinline__ void row_bcast16_impl(float x, float* out, std::integer_sequence<int, J...>) {
-  ((out[J] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xf,
-                                                                   0xf, false))),
+  // Every lane is written (the source lane always exists), so no old value is needed.
+  ((out[J] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf,
+                                                                false))),
    ...);
 }
 __device__ __forceinline__ void row_bcast16(float x, float (&out)[16]) {
