@@ -469,7 +469,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
-                     "kernel": "attn_fwd_pp_kernel (+ the K/V tile prep pass, the tail-split launch and its merge, inside the same timed call)",
+                     "kernel": "attn_fwd_pp_kernel (+ the K/V tile prep pass, the work-counter reset and the merge of the split tiles, inside the same timed call)",
                      "flop_per_launch": fwd_flop},
     }
     result.update(extra)

@@ -130,12 +130,14 @@ int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D,
  * the exponents following as int32 [B, H, ceil(L/64)]) and V transposed as
  * [B, H, ceil(L/64), D, 64] bf16 (the PV product's operand layout); each
  * part starts on a 256-byte boundary.  Large problems add one more part: the
- * kernel runs 256-row query tiles 256 at a time, and when their count
- * n = B*H*ceil(L/256) is at least 1024 and not a multiple of 256, the last
- * t = n % 256 tiles run as S = min(8, 256/t) key ranges each (no split if
- * S < 2), whose fp32 partials ([t*S][256 rows][132 floats]) a merge pass
- * combines exactly; the size function accounts for them.  Its contents on
- * return are unspecified.
+ * kernel runs 256-row query tiles, 256 at a time (one per compute unit), and
+ * the last ones of n = B*H*ceil(L/256) run as S key ranges each, whose fp32
+ * partials ([tiles*S][256 rows][132 floats]) a merge pass combines exactly:
+ * for n >= 2048 the last n % 256 + 256 tiles with S = 4; for 1024 <= n < 2048
+ * the last t = n % 256 with S = min(8, 256/t) (none if t = 0 or S < 2).  The
+ * last 256 bytes hold a counter from which the workgroups take their tiles.
+ * The size function accounts for all of it.  Its contents on return are
+ * unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 

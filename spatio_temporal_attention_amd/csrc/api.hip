@@ -125,6 +125,7 @@ int run_self_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
   p.part = (tail_split && wl.part != 0) ? (float*)((uint8_t*)ws + wl.part) : nullptr;
+  p.work = tail_split ? (int*)((uint8_t*)ws + wl.work) : nullptr;
   return hip_status(launch_attn_fwd_tiled(p, s));
 }
 

@@ -71,6 +71,8 @@ constexpr int PP_BR = 32 * PP_WAVES;   // query rows per workgroup
 static_assert(PP_BR == FWD_ROWS, "the tail split and its workspace assume 256-row workgroups");
 
 // SPLIT: the tail launch (one key range of a query tile, fp32 partial out).
+// The main launch with fixed lengths and 8 waves (UNI below) also runs the
+// pieces itself, as its workgroups from p.n_main_wg on, after the whole tiles.
 // VARLEN: the main launch with variable lengths, where a workgroup whose query
 // tile lies wholly past its item's length leaves at once (an instantiation of
 // its own, so the fixed-length code is unaffected).
@@ -101,12 +103,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const bool late = NW == 8 && wv >= NW / 2;   // waves 4..7: one phase behind
 
-  int logical, split = 0;
+  constexpr bool UNI = !SPLIT && !VARLEN && NW == 8;
+  // With p.work (UNI only), a workgroup's item is not its blockIdx.x but the
+  // next value of the counter at p.work (zero at launch), below p.n_items:
+  // items below p.n_main_wg are whole query tiles (logical order), item
+  // p.n_main_wg + k is piece k; the launch holds more workgroups than items,
+  // and those that find none leave at once.  The XCDs of a chip run at
+  // unequal speeds (a few percent apart), and each receives a fixed share of
+  // a launch's workgroups: with one item each, the slowest XCD ends the
+  // launch, while with items taken in turn the faster ones do more of them.
+  int item = (int)blockIdx.x;
+  const bool counted = UNI && p.work != nullptr;
+  if (counted) {
+    __shared__ int next_item;
+    if (tid == 0) next_item = __hip_atomic_fetch_add(p.work, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(next_item);
+    if (item >= p.n_items) return;   // the whole workgroup: item is uniform
+  }
+  int logical, split = 0, piece_idx = 0;
+  bool piece = SPLIT;
   if (SPLIT) {
-    logical = p.qt_base + (int)blockIdx.x / p.n_split;
-    split = (int)blockIdx.x % p.n_split;
+    piece_idx = item;
+    logical = p.qt_base + piece_idx / p.n_split;
+    split = piece_idx % p.n_split;
+  } else if (UNI && item >= p.n_main_wg) {
+    piece = true;
+    piece_idx = item - p.n_main_wg;
+    logical = p.qt_base + piece_idx / p.n_split;
+    split = piece_idx % p.n_split;
   } else {
-    logical = xcd_remap(blockIdx.x, gridDim.x);
+    logical = counted ? item : xcd_remap(item, UNI ? p.n_main_wg : (int)gridDim.x);
   }
   const int qt = logical % p.n_qtiles;
   const int bh = logical / p.n_qtiles;
@@ -185,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
   const int n_tiles = (n_keys + FWD_BC - 1) / FWD_BC;
   // Key tiles [t_begin, t_end): all of them, or one of p.n_split ranges.
   int t_begin = 0, t_end = n_tiles;
-  if (SPLIT) {
+  if (piece) {
     const int chunk = (n_tiles + p.n_split - 1) / p.n_split;
     t_begin = min(n_tiles, split * chunk);
     t_end = min(n_tiles, t_begin + chunk);
@@ -383,10 +410,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
   }
 
   const float l_tot = xor32_sum(l_run);
-  if (SPLIT) {
+  if (piece) {
     // Partial of this key range: O unnormalized, the running max m (log2
     // units; -inf for an empty range) and l = sum of P against it.
-    float* dst = p.part + ((int64_t)blockIdx.x * BR + wave * 32 + col) * FWD_PART_FLOATS;
+    float* dst = p.part + ((int64_t)piece_idx * BR + wave * 32 + col) * FWD_PART_FLOATS;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -397,10 +424,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
       dst[128] = m_run;
       dst[129] = l_tot;
     }
-    return;
-  }
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (row_ok) {
+  } else if (row_ok) {
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     uint16_t* orow = p.o + ((int64_t)b * p.Lq * p.H + h) * HD + (int64_t)i * q_row_stride;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -418,6 +443,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
     }
   }
 }
+
+// The work counter of the forward starts at zero (a kernel, not a
+// memset: callers may capture the forward in a graph).
+__global__ void fwd_work_reset_kernel(int* work) { *work = 0; }
 
 // Merge of the tail split's partials: per query row, m = max over the key
 // ranges of m_s, l = sum_s l_s 2^(m_s - m), O = sum_s O_s 2^(m_s - m) / l and
@@ -486,15 +515,41 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
   r.n_qtiles = (p.Lq + PP_BR - 1) / PP_BR;
   const int64_t n = (int64_t)r.n_qtiles * p.H * p.B;
   if (n <= 0 || n > 0x7fffffff) return hipErrorInvalidValue;
-  // The tail split follows the rule the workspace was sized by.
+  // Fixed lengths: one launch, whose last workgroups run the split pieces
+  // (fwd_split, the rule the workspace was sized by).  Variable lengths: a
+  // main launch, then the pieces of fwd_tail_split's tail in a launch of
+  // their own.
+  const bool uni = p.q_lens == nullptr;
   FwdSplit sp{(int)n, (int)n, 0, 1};
-  if (p.part != nullptr) sp = fwd_tail_split(p.B, p.Lq, p.H);
+  if (p.part != nullptr) sp = uni ? fwd_split(p.B, p.Lq, p.H) : fwd_tail_split(p.B, p.Lq, p.H);
   if (sp.n != n) return hipErrorInvalidValue;
+  r.n_main_wg = sp.n_main;
+  r.qt_base = sp.n_main;
+  r.n_split = sp.S;
   const bool pos = p.scale_log2 > 0.f;
   const dim3 block(64 * PP_WAVES);
-  if (sp.n_main > 0) {
-    const dim3 grid((unsigned)sp.n_main);
-    if (p.q_lens != nullptr) {
+  if (uni) {
+    const int64_t total = (int64_t)sp.n_main + (int64_t)sp.tail * sp.S;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    r.n_items = (int)total;
+    int64_t wgs = total;
+    if (r.work != nullptr) {
+      // Workgroups take items from the counter: one eighth more of them than
+      // items, so that the faster XCDs find items beyond an even share.
+      wgs = total + (total + 7) / 8;
+      hipLaunchKernelGGL(fwd_work_reset_kernel, dim3(1), dim3(1), 0, stream, r.work);
+    }
+    const dim3 grid((unsigned)wgs);
+    if (pos) {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, false>), grid, block, 0, stream, r);
+    } else {
+      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, false>), grid, block, 0, stream, r);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, false>), grid, block, 0, stream, r);
+    }
+  } else {
+    if (sp.n_main > 0) {
+      const dim3 grid((unsigned)sp.n_main);
       if (pos) {
         if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, true>), grid, block, 0, stream, r);
         else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, true>), grid, block, 0, stream, r);
@@ -502,28 +557,21 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
         if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, true>), grid, block, 0, stream, r);
         else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, true>), grid, block, 0, stream, r);
       }
-    } else if (pos) {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, false>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, false>), grid, block, 0, stream, r);
-    } else {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, false>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, false>), grid, block, 0, stream, r);
+    }
+    if (sp.tail > 0) {
+      const dim3 grid((unsigned)(sp.tail * sp.S));
+      if (pos) {
+        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, true, false>), grid, block, 0, stream, r);
+        else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, true, false>), grid, block, 0, stream, r);
+      } else {
+        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, true, false>), grid, block, 0, stream, r);
+        else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, true, false>), grid, block, 0, stream, r);
+      }
     }
   }
-  if (sp.tail > 0) {
-    r.qt_base = sp.n_main;
-    r.n_split = sp.S;
-    const dim3 grid((unsigned)(sp.tail * sp.S));
-    if (pos) {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, true, false>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, true, false>), grid, block, 0, stream, r);
-    } else {
-      if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, true, false>), grid, block, 0, stream, r);
-      else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, true, false>), grid, block, 0, stream, r);
-    }
+  if (sp.tail > 0)
     hipLaunchKernelGGL(fwd_split_merge_kernel, dim3((unsigned)(sp.tail * (PP_BR * 32 / 256))), dim3(256), 0, stream,
                        r, sp.tail);
-  }
   return hipGetLastError();
 }
 

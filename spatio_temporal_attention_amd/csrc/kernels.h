@@ -31,6 +31,14 @@ struct FwdParams {
   // key ranges (nullptr: no split); qt_base and n_split are set by the launcher.
   float* part;
   int qt_base, n_split;
+  // The main launch with its split pieces at the end (set by the launcher):
+  // workgroups [0, n_main_wg) take whole query tiles, the rest the pieces.
+  int n_main_wg;
+  // Main launch with fixed lengths: a work counter, zero at launch, from which
+  // workgroups take their items, and the number of items (n_main_wg whole
+  // tiles, then the pieces); work == nullptr: workgroup x takes item x.
+  int* work;
+  int n_items;
 };
 
 // Self-attention backward over the prep passes' tiles: [B, H, ceil(L/64)]

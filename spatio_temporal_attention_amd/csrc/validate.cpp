@@ -58,8 +58,18 @@ FwdSplit fwd_tail_split(int B, int Lq, int H) {
   return sp;
 }
 
+FwdSplit fwd_split(int B, int Lq, int H) {
+  FwdSplit sp = fwd_tail_split(B, Lq, H);
+  if ((int64_t)sp.n < 8 * FWD_ROUND) return sp;
+  const int tail = sp.n % FWD_ROUND + FWD_ROUND;
+  sp.n_main = sp.n - tail;
+  sp.tail = tail;
+  sp.S = 4;
+  return sp;
+}
+
 static FwdWsLayout fwd_tiles_layout(int B, int L, int H, int D, int with_rope) {
-  FwdWsLayout w{0, 0, 0, 0, 0};
+  FwdWsLayout w{0, 0, 0, 0, 0, 0};
   if (check_dims(B, L, H, D) != WANATTN_OK) return w;
   const size_t tiles = (size_t)B * H * (((size_t)L + 63) / 64);
   const size_t tile_elems = tiles * 64 * (size_t)D;
@@ -76,11 +86,14 @@ static FwdWsLayout fwd_tiles_layout(int B, int L, int H, int D, int with_rope) {
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
   FwdWsLayout w = fwd_tiles_layout(B, L, H, D, with_rope);
   if (w.total == 0) return w;
-  const FwdSplit sp = fwd_tail_split(B, L, H);
+  const FwdSplit sp = fwd_split(B, L, H);   // covers fwd_tail_split's tail too
   if (sp.tail > 0) {
     w.part = align256(w.total);
     w.total = w.part + (size_t)sp.tail * sp.S * FWD_ROWS * FWD_PART_FLOATS * 4;
   }
+  // The forward's work counter (one int, on 256 bytes of its own).
+  w.work = align256(w.total);
+  w.total = w.work + 256;
   return w;
 }
 

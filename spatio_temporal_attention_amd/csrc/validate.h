@@ -26,6 +26,12 @@ int64_t rope_table_entries(wanattn_grid g, wanattn_rope r);   // (cos, sin) pair
 // round, the last tail = n % FWD_ROUND query tiles would run alone on a few
 // CUs.  They run instead as S = FWD_ROUND / tail (at most 8) key ranges each,
 // whose fp32 partials a merge pass combines exactly.  S < 2: no split.
+// (fwd_tail_split; the backward's dQ and dK/dV passes split their tails by it.)
+// The self-attention forward itself (fwd_split) runs its pieces at the end of
+// the main launch, after the whole query tiles, and from eight rounds on it
+// also splits one more round, 4 key ranges per tile: over tens of rounds the
+// CUs drift apart by about a round, and those that finish their last whole
+// tile early take the pieces instead of idling until the last one finishes.
 constexpr int FWD_ROUND = 256;
 constexpr int FWD_ROWS = 256;          // query rows per forward workgroup
 constexpr int FWD_PART_FLOATS = 132;   // per partial row: O (128, unnormalized), m (log2), l, 2 pad (16-byte rows)
@@ -36,6 +42,7 @@ struct FwdSplit {
   int S;        // key ranges per tail tile
 };
 FwdSplit fwd_tail_split(int B, int Lq, int H);
+FwdSplit fwd_split(int B, int Lq, int H);
 
 // Forward workspace, in 64-key tiles of every (b, h): K (bf16, or with RoPE
 // the rotated keys in fp16 with a power-of-two exponent per tile), V^T
@@ -43,7 +50,7 @@ FwdSplit fwd_tail_split(int B, int Lq, int H);
 // with a tail split only) the fp32 partials [tail * S][FWD_ROWS][132]; each
 // part starts on a 256-byte boundary.
 struct FwdWsLayout {
-  size_t kt, vt, kexp, part, total;   // byte offsets of the parts and the total size (part: 0 if none)
+  size_t kt, vt, kexp, part, work, total;   // byte offsets of the parts and the total size (part, work: 0 if none)
 };
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope);
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);

@@ -19,6 +19,13 @@ H_API void h_fwd_tail_split(int B, int Lq, int H, int* out) {
   out[2] = s.tail;
   out[3] = s.S;
 }
+H_API void h_fwd_split(int B, int Lq, int H, int* out) {
+  const FwdSplit s = fwd_split(B, Lq, H);
+  out[0] = s.n;
+  out[1] = s.n_main;
+  out[2] = s.tail;
+  out[3] = s.S;
+}
 H_API int h_bwd_q_split(int B, int Lq, int Lk, int H) { return bwd_q_split(B, Lq, Lk, H); }
 H_API size_t h_self_fwd_ws_bytes(int B, int L, int H, int D, int rope) { return self_fwd_ws_bytes(B, L, H, D, rope); }
 H_API size_t h_fwd_tiles_ws_bytes(int B, int L, int H, int D, int rope) { return fwd_tiles_ws_bytes(B, L, H, D, rope); }

@@ -4,7 +4,9 @@ The forward and the backward's dQ pass run 256-row query blocks, the dK/dV
 passes 256-key blocks, 256 at a time; when a large problem's block count n is
 not a multiple of 256, the last n % 256 blocks run as several key (or query)
 ranges each, whose fp32 partials are combined after (the forward merges softmax
-partials exactly; the backward sums its partials in range order).  These shapes
+partials exactly; the backward sums its partials in range order).  The
+fixed-length forward runs its pieces as the last workgroups of its main launch
+and, from eight rounds on, splits one more round too.  These shapes
 put the split on known heads (logical block = (head * B + item) *
 blocks_per_head + block, batch item innermost) and check those heads in full;
 same bar as the other parity tests (max-abs 2e-2, rel-L2 5e-3 on O, dQ, dK, dV;
@@ -58,6 +60,35 @@ def test_tail_split_heads_match_oracle():
     torch.cuda.synchronize()
     go, gl = bf16_to_f64(o), f32_to_np(lse)
     heads = [128, 129, 0]                          # the two split heads, and one of the main launch
+    f = synth.bf16_bits_to_f64
+    ro, rl = oracle.self_fwd_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), SCALE, GRID, ROPE)
+    for j, h in enumerate(heads):
+        print(f"  head {h}:")
+        check_close("O", go[:, :, h], ro[:, :, j])
+        check_lse("LSE", gl[:, h], rl[:, j])
+
+
+def _fwd_split_rule(B, L, H):
+    """The self-attention forward's own split: from eight rounds on, the last n % 256 tiles and one more round
+    run as 4 key ranges each, as the last workgroups of the same launch."""
+    n = B * H * ((L + 255) // 256)
+    if n < 2048:
+        return _split_rule(B, L, H)
+    tail = n % 256 + 256
+    return n - tail, tail, 4
+
+
+def test_forward_split_extra_round_heads_match_oracle():
+    B, H = 1, 272                                  # 2,176 query tiles: 8.5 rounds
+    L = int(np.prod(GRID))
+    n_main, tail, S = _fwd_split_rule(B, L, H)
+    assert (n_main, tail, S) == (1792, 384, 4)     # heads 224..271 run as 4 key ranges of 8 tiles each
+    q, k, v = (synth.random_bf16(9150 + i, (B, L, H, 128)) for i in range(3))
+    o, lse = wa.self_fwd(to_dev(q), to_dev(k), to_dev(v), grid=GRID, table=wa.rope_table(GRID, ROPE), rope=ROPE,
+                         scale=SCALE)
+    torch.cuda.synchronize()
+    go, gl = bf16_to_f64(o), f32_to_np(lse)
+    heads = [223, 224, 250, 271]                   # the last whole-tile head, then split heads
     f = synth.bf16_bits_to_f64
     ro, rl = oracle.self_fwd_ref(f(q[:, :, heads]), f(k[:, :, heads]), f(v[:, :, heads]), SCALE, GRID, ROPE)
     for j, h in enumerate(heads):

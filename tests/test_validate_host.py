@@ -39,6 +39,7 @@ SIGS = {
     "h_check_scale": (_i, [_f]),
     "h_rope_table_entries": (ctypes.c_longlong, [Grid, Rope]),
     "h_fwd_tail_split": (None, [_i, _i, _i, ctypes.POINTER(_i)]),
+    "h_fwd_split": (None, [_i, _i, _i, ctypes.POINTER(_i)]),
     "h_bwd_q_split": (_i, [_i, _i, _i, _i]),
     "h_self_fwd_ws_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "h_fwd_tiles_ws_bytes": (_sz, [_i, _i, _i, _i, _i]),
@@ -120,6 +121,17 @@ def test_split_rules(h):
     assert list(out) == [1200, 1200, 0, 1]                          # tail 176: S = 1 < 2, no split
     h.h_fwd_tail_split(1, 2048, 130, out)
     assert list(out) == [1040, 1024, 16, 8]                         # S capped at 8
+    # the forward's own split: from eight rounds on, one more round of tiles as 4 key ranges each
+    h.h_fwd_split(1, L720, H720, out)
+    assert list(out) == [11840, 11520, 320, 4]
+    h.h_fwd_split(1, L720, 32, out)
+    assert list(out) == [9472, 9216, 256, 4]                        # a whole number of rounds: the last one
+    h.h_fwd_split(1, 2048, 255, out)
+    assert list(out) == [2040, 2040, 0, 1]                          # under eight rounds: fwd_tail_split's rule
+    h.h_fwd_split(1, 2048, 130, out)
+    assert list(out) == [1040, 1024, 16, 8]
+    h.h_fwd_split(1, 2048, 256, out)
+    assert list(out) == [2048, 1792, 256, 4]                        # eight rounds exactly
     assert h.h_bwd_q_split(1, L720, L720, H720) == 1                # 11,840 key blocks fill the chip
     assert h.h_bwd_q_split(1, L720, 512, H720) == 16                # 80 key blocks: 1,280 workgroups, 5 full rounds
     assert h.h_bwd_q_split(2, 32760, 512, 12) == 16                 # 48 key blocks: 768 workgroups, 3 full rounds
@@ -130,9 +142,9 @@ def test_workspace_sizes(h):
     up = lambda x: (x + 255) // 256 * 256
     tiles = 40 * ((L720 + 63) // 64)
     tile_bytes = tiles * 64 * 128 * 2
-    part = 64 * 4 * 256 * 132 * 4
-    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 1) == up(up(2 * tile_bytes) + 4 * tiles) + part
-    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 0) == up(2 * tile_bytes) + part
+    part = (64 + 256) * 4 * 256 * 132 * 4   # the forward's split: the last 64 tiles and one more round
+    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 1) == up(up(2 * tile_bytes) + 4 * tiles) + part + 256
+    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 0) == up(2 * tile_bytes) + part + 256
     assert h.h_fwd_tiles_ws_bytes(1, L720, H720, 128, 1) == up(2 * tile_bytes) + 4 * tiles
     assert h.h_self_fwd_ws_bytes(1, L720, H720, 64, 1) == 0         # invalid shapes size to 0
     assert h.h_self_bwd_ws_bytes(1, L720, H720, 128, 1) == h.h_cross_bwd_ws_bytes(1, L720, L720, H720, 128)
