@@ -129,15 +129,15 @@ int wanattn_rope3d(const void* x, void* y, int B, int L, int H, int D,
  * a table the rotated keys in fp16 with one power-of-two exponent per tile,
  * the exponents following as int32 [B, H, ceil(L/64)]) and V transposed as
  * [B, H, ceil(L/64), D, 64] bf16 (the PV product's operand layout); each
- * part starts on a 256-byte boundary.  Large problems add one more part: the
- * kernel runs 256-row query tiles, 256 at a time (one per compute unit), and
- * the last ones of n = B*H*ceil(L/256) run as S key ranges each, whose fp32
- * partials ([tiles*S][256 rows][132 floats]) a merge pass combines exactly:
- * for n >= 2048 the last n % 256 + 256 tiles with S = 4; for 1024 <= n < 2048
- * the last t = n % 256 with S = min(8, 256/t) (none if t = 0 or S < 2).  The
- * last 256 bytes hold a counter from which the workgroups take their tiles.
- * The size function accounts for all of it.  Its contents on return are
- * unspecified.
+ * part starts on a 256-byte boundary.  Then 256 bytes hold a counter from
+ * which the workgroups take their query tiles.  Large problems add one more
+ * part: the kernel runs 256-row query tiles, 256 at a time (one per compute
+ * unit), and the last ones of n = B*H*ceil(L/256) run as S key ranges each,
+ * whose fp32 partials ([tiles*S][256 rows][132 floats]) a merge pass combines
+ * exactly: for n >= 2048 the last n % 256 + 256 tiles with S = 4; for
+ * 1024 <= n < 2048 the last t = n % 256 with S = min(8, 256/t) (none if t = 0
+ * or S < 2).  The size function accounts for all of it.  Its contents on
+ * return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_fwd_workspace_bytes(int B, int L, int H, int D, int with_rope);
 
@@ -159,7 +159,8 @@ int wanattn_self_fwd(const void* q, const void* k, const void* v, void* o, float
  * up to P's e4m3 rounding (relative L2 of a few 1e-2 on flat rows); LSE to
  * ~1e-4.  Workspace (required, 16-byte aligned):
  * wanattn_self_fwd_fp8_workspace_bytes(B, L, H, D): e4m3 K and V^T tiles
- * ([B, H, ceil(L/64)] x 8 KB each) and their int32 exponents.
+ * ([B, H, ceil(L/64)] x 8 KB each), their int32 exponents and a 256-byte
+ * counter from which the workgroups take their query tiles.
  * ------------------------------------------------------------------------- */
 size_t wanattn_self_fwd_fp8_workspace_bytes(int B, int L, int H, int D);
 
@@ -232,7 +233,7 @@ int wanattn_self_fwd_varlen(const void* q, const void* k, const void* v, void* o
  * shard's keys only; wanattn_lse_merge combines the shards exactly.  table ==
  * NULL: no rotation (g and the offsets only need to be >= 0).
  * Workspace: wanattn_partial_fwd_workspace_bytes(B, Lk, H, D, table != NULL):
- * the key/value tiles only (no tail split).
+ * the key/value tiles and the 256-byte work counter (no tail split).
  * ------------------------------------------------------------------------- */
 size_t wanattn_partial_fwd_workspace_bytes(int B, int Lk, int H, int D, int with_rope);
 
@@ -265,9 +266,10 @@ int wanattn_lse_merge(const void* const* o_parts, const float* const* lse_parts,
  * Workspace (required, 16-byte aligned): wanattn_cross_fwd_workspace_bytes(B,
  * Lk, H, D) bytes.  It receives the text keys and values rewritten in 64-key
  * tiles of every (b, h): K as [B, H, ceil(Lk/64), 64, D] bf16 and V
- * transposed as [B, H, ceil(Lk/64), D, 64] bf16, keys past k_lens[b] zero;
- * each part starts on a 256-byte boundary (10.5 MB at Lk = 512, H = 40).  Its
- * contents on return are unspecified.
+ * transposed as [B, H, ceil(Lk/64), D, 64] bf16, keys past k_lens[b] zero,
+ * then 256 bytes the kernel does not use here (the layout is the partial
+ * forward's); each part starts on a 256-byte boundary (10.5 MB at Lk = 512,
+ * H = 40).  Its contents on return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_cross_fwd_workspace_bytes(int B, int Lk, int H, int D);
 

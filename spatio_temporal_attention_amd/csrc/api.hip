@@ -125,7 +125,7 @@ int run_self_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
   p.part = (tail_split && wl.part != 0) ? (float*)((uint8_t*)ws + wl.part) : nullptr;
-  p.work = tail_split ? (int*)((uint8_t*)ws + wl.work) : nullptr;
+  p.work = (int*)((uint8_t*)ws + wl.work);   // right after the tiles in every forward workspace layout
   return hip_status(launch_attn_fwd_tiled(p, s));
 }
 
@@ -221,6 +221,7 @@ WANATTN_API int wanattn_self_fwd_fp8(const void* q, const void* k, const void* v
   p.Lk = L;
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
+  p.work = (int*)(base + w.work);
   return hip_status(launch_attn_fwd_fp8(p, base + w.k8, (const int*)(base + w.kexp), base + w.v8,
                                         (const int*)(base + w.vexp), s));
 }

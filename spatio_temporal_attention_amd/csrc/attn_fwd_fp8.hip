@@ -186,7 +186,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(FwdParams p, const
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  // The workgroup's query tile: from the work counter (common.h), or blockIdx.x remapped.
+  int logical;
+  if (p.work != nullptr) {
+    logical = take_work_item(p.work);
+    if (logical >= p.n_items) return;   // the whole workgroup: the value is uniform
+  } else {
+    logical = xcd_remap(blockIdx.x, gridDim.x);
+  }
   const int qt = logical % p.n_qtiles;
   const int bh = logical / p.n_qtiles;
   const int b = bh % p.B;   // batch innermost: every XCD gets the same heads of every item
@@ -455,11 +462,17 @@ hipError_t launch_attn_fwd_fp8(const FwdParams& p, const uint8_t* k8, const int*
   const int64_t total = (int64_t)q.n_qtiles * p.H * p.B;
   if (total <= 0 || total > 0x7fffffff || p.Lq != p.Lk) return hipErrorInvalidValue;
   if ((int64_t)((p.Lk + F8_BC - 1) / F8_BC) * F8_TILE_BYTES > (int64_t)0xffffffff) return hipErrorInvalidValue;
+  q.n_items = (int)total;
+  int64_t wgs = total;
+  if (q.work != nullptr) {
+    wgs = work_grid(total);
+    hipLaunchKernelGGL(work_reset_kernel, dim3(1), dim3(1), 0, stream, q.work);
+  }
   if (p.scale_log2 > 0.f)
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true>), dim3((unsigned)total), dim3(256), 0, stream, q, k8, kexp, v8,
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<true>), dim3((unsigned)wgs), dim3(256), 0, stream, q, k8, kexp, v8,
                        vexp);
   else
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false>), dim3((unsigned)total), dim3(256), 0, stream, q, k8, kexp, v8,
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<false>), dim3((unsigned)wgs), dim3(256), 0, stream, q, k8, kexp, v8,
                        vexp);
   return hipGetLastError();
 }

@@ -104,21 +104,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
   const bool late = NW == 8 && wv >= NW / 2;   // waves 4..7: one phase behind
 
   constexpr bool UNI = !SPLIT && !VARLEN && NW == 8;
-  // With p.work (UNI only), a workgroup's item is not its blockIdx.x but the
-  // next value of the counter at p.work (zero at launch), below p.n_items:
-  // items below p.n_main_wg are whole query tiles (logical order), item
-  // p.n_main_wg + k is piece k; the launch holds more workgroups than items,
-  // and those that find none leave at once.  The XCDs of a chip run at
-  // unequal speeds (a few percent apart), and each receives a fixed share of
-  // a launch's workgroups: with one item each, the slowest XCD ends the
-  // launch, while with items taken in turn the faster ones do more of them.
+  // With p.work (the main launches, fixed or variable lengths) the workgroup
+  // takes its item from that counter (take_work_item), below p.n_items: items
+  // below p.n_main_wg are whole query tiles (logical order), item
+  // p.n_main_wg + k is piece k (fixed lengths only).
   int item = (int)blockIdx.x;
-  const bool counted = UNI && p.work != nullptr;
+  const bool counted = !SPLIT && NW == 8 && p.work != nullptr;
   if (counted) {
-    __shared__ int next_item;
-    if (tid == 0) next_item = __hip_atomic_fetch_add(p.work, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(next_item);
+    item = take_work_item(p.work);
     if (item >= p.n_items) return;   // the whole workgroup: item is uniform
   }
   int logical, split = 0, piece_idx = 0;
@@ -444,10 +437,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
   }
 }
 
-// The work counter of the forward starts at zero (a kernel, not a
-// memset: callers may capture the forward in a graph).
-__global__ void fwd_work_reset_kernel(int* work) { *work = 0; }
-
 // Merge of the tail split's partials: per query row, m = max over the key
 // ranges of m_s, l = sum_s l_s 2^(m_s - m), O = sum_s O_s 2^(m_s - m) / l and
 // LSE = ln 2 (m + log2 l) (fixed order over s).  One thread per row and four
@@ -534,10 +523,8 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
     r.n_items = (int)total;
     int64_t wgs = total;
     if (r.work != nullptr) {
-      // Workgroups take items from the counter: one eighth more of them than
-      // items, so that the faster XCDs find items beyond an even share.
-      wgs = total + (total + 7) / 8;
-      hipLaunchKernelGGL(fwd_work_reset_kernel, dim3(1), dim3(1), 0, stream, r.work);
+      wgs = work_grid(total);
+      hipLaunchKernelGGL(work_reset_kernel, dim3(1), dim3(1), 0, stream, r.work);
     }
     const dim3 grid((unsigned)wgs);
     if (pos) {
@@ -549,13 +536,20 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
     }
   } else {
     if (sp.n_main > 0) {
-      const dim3 grid((unsigned)sp.n_main);
+      FwdParams m = r;
+      m.n_items = sp.n_main;
+      int64_t wgs = sp.n_main;
+      if (m.work != nullptr) {
+        wgs = work_grid(sp.n_main);
+        hipLaunchKernelGGL(work_reset_kernel, dim3(1), dim3(1), 0, stream, m.work);
+      }
+      const dim3 grid((unsigned)wgs);
       if (pos) {
-        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, true>), grid, block, 0, stream, r);
-        else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, true>), grid, block, 0, stream, r);
+        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<true, true, false, true>), grid, block, 0, stream, m);
+        else hipLaunchKernelGGL((attn_fwd_pp_kernel<true, false, false, true>), grid, block, 0, stream, m);
       } else {
-        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, true>), grid, block, 0, stream, r);
-        else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, true>), grid, block, 0, stream, r);
+        if (f16) hipLaunchKernelGGL((attn_fwd_pp_kernel<false, true, false, true>), grid, block, 0, stream, m);
+        else hipLaunchKernelGGL((attn_fwd_pp_kernel<false, false, false, true>), grid, block, 0, stream, m);
       }
     }
     if (sp.tail > 0) {

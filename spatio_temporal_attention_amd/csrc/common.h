@@ -306,4 +306,29 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// Work counter.  The XCDs of a chip run at unequal speeds (a few percent
+// apart), yet each receives a fixed eighth of a launch's workgroups (workgroup
+// x on XCD x % 8), so with one fixed item per workgroup the slowest XCD ends
+// the launch.  Instead the workgroups take their items from a counter, in the
+// order of the items' index, and the launch holds work_grid(n) workgroups for
+// n items: the faster XCDs go on to their spare workgroups and take more
+// items, and workgroups that draw a value past the last item leave at once.
+__host__ __device__ constexpr int64_t work_grid(int64_t n_items) { return n_items + (n_items + 7) / 8; }
+
+// The workgroup's item (the counter's next value): its first thread draws it
+// and shares it through LDS.  Every thread of the workgroup calls it, before
+// any other barrier.
+__device__ __forceinline__ int take_work_item(int* work) {
+  __shared__ int drawn;
+  if (threadIdx.x == 0) drawn = __hip_atomic_fetch_add(work, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(drawn);
+}
+
+// The counter starts at zero: a kernel rather than a memset, so that callers
+// may capture the launches in a graph.
+namespace {   // one copy per translation unit
+__global__ void work_reset_kernel(int* work) { *work = 0; }
+}  // namespace
+
 }  // namespace wanattn

@@ -80,6 +80,9 @@ static FwdWsLayout fwd_tiles_layout(int B, int L, int H, int D, int with_rope) {
     w.kexp = w.total;                         // exponent of every K tile, int32 [B, H, tile]
     w.total = w.kexp + tiles * 4;
   }
+  // The main launch's work counter (one int, on 256 bytes of its own).
+  w.work = align256(w.total);
+  w.total = w.work + 256;
   return w;
 }
 
@@ -91,9 +94,6 @@ FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope) {
     w.part = align256(w.total);
     w.total = w.part + (size_t)sp.tail * sp.S * FWD_ROWS * FWD_PART_FLOATS * 4;
   }
-  // The forward's work counter (one int, on 256 bytes of its own).
-  w.work = align256(w.total);
-  w.total = w.work + 256;
   return w;
 }
 
@@ -113,7 +113,8 @@ Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D) {
   w.v8 = align256(tiles * 64 * (size_t)D);
   w.kexp = align256(w.v8 + tiles * 64 * (size_t)D);
   w.vexp = align256(w.kexp + tiles * 4);
-  w.total = w.vexp + tiles * 4;
+  w.work = align256(w.vexp + tiles * 4);   // the work counter (one int, on 256 bytes of its own)
+  w.total = w.work + 256;
   return w;
 }
 

@@ -46,20 +46,21 @@ FwdSplit fwd_split(int B, int Lq, int H);
 
 // Forward workspace, in 64-key tiles of every (b, h): K (bf16, or with RoPE
 // the rotated keys in fp16 with a power-of-two exponent per tile), V^T
-// (bf16), then with RoPE the tile exponents (int32), then (self-attention
-// with a tail split only) the fp32 partials [tail * S][FWD_ROWS][132]; each
-// part starts on a 256-byte boundary.
+// (bf16), then with RoPE the tile exponents (int32), then the main launch's
+// work counter (256 bytes), then (self-attention with a tail split only) the
+// fp32 partials [tail * S][FWD_ROWS][132]; each part starts on a 256-byte
+// boundary.
 struct FwdWsLayout {
-  size_t kt, vt, kexp, part, work, total;   // byte offsets of the parts and the total size (part, work: 0 if none)
+  size_t kt, vt, kexp, part, work, total;   // byte offsets of the parts and the total size (part: 0 if none)
 };
 FwdWsLayout self_fwd_ws_layout(int B, int L, int H, int D, int with_rope);
 size_t self_fwd_ws_bytes(int B, int L, int H, int D, int with_rope);
 // The key/value tiles alone (the shard forward, whose query and key lengths differ, takes no split).
 size_t fwd_tiles_ws_bytes(int B, int L, int H, int D, int with_rope);
 // FP8 forward workspace: K and V^T e4m3 tiles ([B, H, ceil(L/64)] x 8 KB each), then
-// their int32 exponents; each part on a 256-byte boundary.
+// their int32 exponents, then the work counter (256 bytes); each part on a 256-byte boundary.
 struct Fp8WsLayout {
-  size_t k8, v8, kexp, vexp, total;
+  size_t k8, v8, kexp, vexp, work, total;
 };
 Fp8WsLayout self_fwd_fp8_ws_layout(int B, int L, int H, int D);
 // Backward workspace: the row statistics of every query tile (fp32

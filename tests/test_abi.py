@@ -66,14 +66,15 @@ def test_workspace_sizes(lib):
     assert tiled > n
     n_tiles = B * H * ((L + 63) // 64)
     # 11,840 query tiles of 256 rows = 46 rounds of 256 + 64: the last 64 and one more round (320 tiles) run
-    # as 4 key ranges each, whose fp32 partials (rows of 132 floats) follow the tiles on a 256-byte boundary
+    # as 4 key ranges each, whose fp32 partials (rows of 132 floats) follow the tiles and the main launch's
+    # work counter (256 bytes), each on a 256-byte boundary
     part = (64 + 256) * 4 * 256 * 132 * 4
     up = lambda x: (x + 255) // 256 * 256
-    # then the persistent launch's work counter on 256 bytes of its own
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == up(2 * tiled * 2) + part + 256
-    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == up(2 * tiled * 2 + 4 * n_tiles) + part + 256
-    assert lib.wanattn_partial_fwd_workspace_bytes(B, L, H, D, 0) == 2 * tiled * 2          # K and V^T tiles
-    assert lib.wanattn_partial_fwd_workspace_bytes(B, L, H, D, 1) == 2 * tiled * 2 + 4 * n_tiles  # + exponents
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 0) == up(2 * tiled * 2) + 256 + part
+    assert lib.wanattn_self_fwd_workspace_bytes(B, L, H, D, 1) == up(2 * tiled * 2 + 4 * n_tiles) + 256 + part
+    # K and V^T tiles (+ exponents), then the counter
+    assert lib.wanattn_partial_fwd_workspace_bytes(B, L, H, D, 0) == up(2 * tiled * 2) + 256
+    assert lib.wanattn_partial_fwd_workspace_bytes(B, L, H, D, 1) == up(2 * tiled * 2 + 4 * n_tiles) + 256
     assert lib.wanattn_self_fwd_workspace_bytes(1, 1, 1, D, 0) == 2 * 64 * D * 2 + 256
     # a multiple of 256 tiles (32 heads: 9,472 = 37 x 256) still splits its last round; no split below four
     # rounds
@@ -192,8 +193,8 @@ def test_cross_and_rope_validation(lib):
     assert cross(kl=P + 1) == ALIGN
     assert cross(scale=float("nan")) == UNSUP
     need = lib.wanattn_cross_fwd_workspace_bytes(2, 512, 2, 128)
-    assert need == 2 * (2 * 2 * 8 * 64 * 128 * 2)                       # K and V^T tiles, 8 per (b, h)
-    assert lib.wanattn_cross_fwd_workspace_bytes(1, 336, 40, 128) == 2 * 40 * 6 * 64 * 128 * 2
+    assert need == 2 * (2 * 2 * 8 * 64 * 128 * 2) + 256                 # K and V^T tiles, 8 per (b, h); 256 bytes
+    assert lib.wanattn_cross_fwd_workspace_bytes(1, 336, 40, 128) == 2 * 40 * 6 * 64 * 128 * 2 + 256
     assert cross(ws=None) == WS
     assert cross(ws_bytes=need - 1) == WS
     assert cross(ws=ODD) == ALIGN
@@ -250,9 +251,9 @@ def test_varlen_partial_merge_validation(lib):
     assert partial(table=ODD) == ALIGN
     assert partial(ws_bytes=lib.wanattn_partial_fwd_workspace_bytes(1, 64, 2, 128, 1) - 1) == WS
     assert partial(v=None) == NULL
-    # the same tiles; the self-attention forward adds its 256-byte work counter
-    tiles_only = lib.wanattn_partial_fwd_workspace_bytes(1, 64, 2, 128, 1)
-    assert (tiles_only + 255) // 256 * 256 + 256 == lib.wanattn_self_fwd_workspace_bytes(1, 64, 2, 128, 1)
+    # the same layout: tiles and counter (no split at this size)
+    assert lib.wanattn_partial_fwd_workspace_bytes(1, 64, 2, 128, 1) == lib.wanattn_self_fwd_workspace_bytes(
+        1, 64, 2, 128, 1)
 
     def merge(R=2, parts=None, lparts=None, o=P, lse=P, B=1, L=70, H=2):
         arr = ctypes.c_void_p * max(R, 1)
@@ -300,7 +301,8 @@ def test_fp8_validation(lib):
         return lib.wanattn_self_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["L"], a["H"], a["D"],
                                         a["g"], a["r"], a["table"], a["scale"], a["ws"], a["ws_bytes"], None)
     need = lib.wanattn_self_fwd_fp8_workspace_bytes(1, 320, 2, 128)
-    assert need == 2 * 10 * 8192 + 256 + 4 * 10   # K and V^T e4m3 tiles, then the two exponent arrays
+    # K and V^T e4m3 tiles, then the two exponent arrays, then the work counter (256 bytes)
+    assert need == 2 * 10 * 8192 + 256 + 256 + 256
     assert f8(ws_bytes=need - 1) == WS
     assert f8(ws=None) == WS
     assert f8(q=None) == NULL

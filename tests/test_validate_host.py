@@ -143,9 +143,10 @@ def test_workspace_sizes(h):
     tiles = 40 * ((L720 + 63) // 64)
     tile_bytes = tiles * 64 * 128 * 2
     part = (64 + 256) * 4 * 256 * 132 * 4   # the forward's split: the last 64 tiles and one more round
-    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 1) == up(up(2 * tile_bytes) + 4 * tiles) + part + 256
-    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 0) == up(2 * tile_bytes) + part + 256
-    assert h.h_fwd_tiles_ws_bytes(1, L720, H720, 128, 1) == up(2 * tile_bytes) + 4 * tiles
+    # the tiles (+ exponents), the work counter (256 bytes), then the split's partials
+    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 1) == up(up(2 * tile_bytes) + 4 * tiles) + 256 + part
+    assert h.h_self_fwd_ws_bytes(1, L720, H720, 128, 0) == up(2 * tile_bytes) + 256 + part
+    assert h.h_fwd_tiles_ws_bytes(1, L720, H720, 128, 1) == up(up(2 * tile_bytes) + 4 * tiles) + 256
     assert h.h_self_fwd_ws_bytes(1, L720, H720, 64, 1) == 0         # invalid shapes size to 0
     assert h.h_self_bwd_ws_bytes(1, L720, H720, 128, 1) == h.h_cross_bwd_ws_bytes(1, L720, L720, H720, 128)
     assert h.h_cross_bwd_ws_bytes(1, L720, 512, H720, 128) > h.h_cross_bwd_ws_bytes(1, 256, 512, H720, 128)
