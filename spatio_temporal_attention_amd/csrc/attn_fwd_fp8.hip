@@ -465,6 +465,7 @@ hipError_t launch_attn_fwd_fp8(const FwdParams& p, const uint8_t* k8, const int*
   q.n_items = (int)total;
   int64_t wgs = total;
   if (q.work != nullptr) {
+    if (!work_fits(total)) return hipErrorInvalidValue;
     wgs = work_grid(total);
     hipLaunchKernelGGL(work_reset_kernel, dim3(1), dim3(1), 0, stream, q.work);
   }

@@ -523,6 +523,7 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
     r.n_items = (int)total;
     int64_t wgs = total;
     if (r.work != nullptr) {
+      if (!work_fits(total)) return hipErrorInvalidValue;
       wgs = work_grid(total);
       hipLaunchKernelGGL(work_reset_kernel, dim3(1), dim3(1), 0, stream, r.work);
     }
@@ -540,6 +541,7 @@ hipError_t launch_attn_fwd_tiled(const FwdParams& p, hipStream_t stream) {
       m.n_items = sp.n_main;
       int64_t wgs = sp.n_main;
       if (m.work != nullptr) {
+        if (!work_fits(sp.n_main)) return hipErrorInvalidValue;
         wgs = work_grid(sp.n_main);
         hipLaunchKernelGGL(work_reset_kernel, dim3(1), dim3(1), 0, stream, m.work);
       }

@@ -313,7 +313,10 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 // order of the items' index, and the launch holds work_grid(n) workgroups for
 // n items: the faster XCDs go on to their spare workgroups and take more
 // items, and workgroups that draw a value past the last item leave at once.
+// The counter is an int and reaches work_grid(n) - 1: launchers refuse a
+// launch whose work_grid exceeds INT_MAX (work_fits).
 __host__ __device__ constexpr int64_t work_grid(int64_t n_items) { return n_items + (n_items + 7) / 8; }
+__host__ __device__ constexpr bool work_fits(int64_t n_items) { return work_grid(n_items) <= 0x7fffffff; }
 
 // The workgroup's item (the counter's next value): its first thread draws it
 // and shares it through LDS.  Every thread of the workgroup calls it, before
