@@ -48,9 +48,9 @@ using namespace bwd;
 // B operands of S = Q K^T and of dP - Delta = dO V^T - Delta, whose
 // accumulator starts at -Delta) and accumulates dK~^T += (R q)^T dS with dS
 // taken from the accumulators.  A lane holds 16 query rows of each 32-row
-// block; their statistics reach it from the lane of its 16-lane row that
-// read them (DPP row broadcast), so one 16-byte LDS read per lane and tile
-// carries them all.
+// block, in four runs of 4 consecutive rows shared by its half of the wave;
+// the statistics are stored by row, so each run's LSE or -Delta is one
+// 16-byte LDS read that the half's lanes share (a broadcast).
 //
 // Ping-pong, as in the forward: each wave alternates a products phase M(u)
 // (MFMA: dK~ += (R q)^T dS of query tile u-1, then S and dP of tile u) and a
@@ -107,7 +107,10 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
   for (int s = 0; s < 8; ++s) rf[s] = DK_QD + col * 256 + (((2 * s + half) ^ swz(col)) << 4);
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) tf[kg] = DK_QT + col * 128 + (((2 * kg + half) ^ swz8(col)) << 4);
-  const uint32_t sf = DK_ST + 16 * (16 * half + (lane & 15));
+  // Statistics (LSE log2 e, then -Delta, by row): this lane's rows of value
+  // group jg in row block qb are 32 qb + 8 jg + 4 half + 0..3, one 16-byte
+  // read that every lane of the half shares (an LDS broadcast).
+  const uint32_t sf = DK_ST + 16 * half;
   auto frag = [&](uint32_t off) __attribute__((always_inline)) { return *reinterpret_cast<const bf16x8*>(smem + off); };
   auto stat4 = [&](uint32_t off) __attribute__((always_inline)) { return *reinterpret_cast<const f32x4*>(smem + off); };
 
@@ -181,11 +184,14 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
       const int t = ks.t0 + u;
       if (SDP && !late) copies(parity, u);
       if (!KMASK || ks.wave_live) {
-        // -Delta of the accumulator's rows: {LSE log2 e, -Delta} x 2 blocks per entry; read first, so that
-        // its wait does not drain the fragment reads queued behind it
-        f32x4 st = f32x4{};
+        // -Delta of the accumulator's rows, read first, so that its wait does not drain the fragment reads
+        // queued behind it
+        f32x4 nd[2][4];
         if (SDP) {
-          st = stat4(sf + 1024 * (t & 3));
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int jg = 0; jg < 4; ++jg) nd[qb][jg] = stat4(sf + 1024 * (t & 3) + 256 + 4 * (32 * qb + 8 * jg));
           __builtin_amdgcn_sched_barrier(0);
         }
         if (GRAD) {
@@ -196,14 +202,11 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
               dk_acc[d] = mfma32(frag(tf[kg] + 16384 * (P ^ 1) + 4096 * d), dsf[kg], dk_acc[d]);
         }
         if (SDP) {
-          float nd[2][16];
-          row_bcast16(st[1], nd[0]);
-          row_bcast16(st[3], nd[1]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
             s_acc[qb] = f32x16{};
 #pragma unroll
-            for (int j = 0; j < 16; ++j) dp_acc[qb][j] = nd[qb][j];
+            for (int j = 0; j < 16; ++j) dp_acc[qb][j] = nd[qb][j >> 2][j & 3];
           }
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
@@ -230,13 +233,17 @@ __global__ __launch_bounds__(64 * DK_WAVES, 1) __attribute__((amdgpu_waves_per_e
       const int t = ks.t0 + u;
       if (late && u + 1 < n) copies(std::integral_constant<int, decltype(parity)::value ^ 1>{}, u + 1);
       if (!KMASK || ks.wave_live) {
-        const f32x4 st = stat4(sf + 1024 * (t & 3));
         const int e_q = *reinterpret_cast<const int*>(smem + DK_ST + 1024 * (t & 3) + 512);
         const float g = ldexpf(p.scale_log2, e_q + e_k);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           float l2[16], dsv[16];
-          row_bcast16(qb ? st[2] : st[0], l2);
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const f32x4 x = stat4(sf + 1024 * (t & 3) + 4 * (32 * qb + 8 * jg));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l2[4 * jg + i] = x[i];
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[qb][j], g, -l2[j]));
@@ -430,12 +437,11 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) __attribute__((amdgpu_waves_per_e
   load_row_frags(qf, p.qf + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
   load_row_frags(dof, p.dor + (tile0 + (tile_ok ? qtile : 0)) * TILE_ELEMS, 32 * (wave & 1) + col, half, tile_ok);
   const int e_q = tile_ok ? p.qexp[tile0 + qtile] : 0;
-  // LSE_i log2 e (+inf past Lq or with no valid key: P = 0) and -Delta_i, from the query prep pass
-  // (row r = 32 (wave % 2) + col of the tile sits in entry 16 ((r / 4) % 2) + 4 ((r / 8) % 4) + r % 4)
-  const float* st = p.qstat + (tile0 + (tile_ok ? qtile : 0)) * QSTAT_FLOATS +
-                    4 * (16 * ((col >> 2) & 1) + 4 * ((col >> 3) & 3) + (col & 3)) + 2 * (wave & 1);
+  // LSE_i log2 e (+inf past Lq or with no valid key: P = 0) and -Delta_i of row r = 32 (wave % 2) + col of
+  // the tile, from the query prep pass (floats r and 64 + r of the tile's statistics)
+  const float* st = p.qstat + (tile0 + (tile_ok ? qtile : 0)) * QSTAT_FLOATS + 32 * (wave & 1) + col;
   const float lse2 = tile_ok ? st[0] : INFINITY;
-  const float ndelta = tile_ok ? st[1] : 0.f;
+  const float ndelta = tile_ok ? st[TILE_ROWS] : 0.f;
 
   f32x16 dq_acc[4];
 #pragma unroll

@@ -20,8 +20,8 @@ using namespace bwd;
 // row statistics.  S = Q K^T from the wave's K rows in registers, dV^T +=
 // dO^T P with P from the accumulators.  The same ping-pong as the dK pass
 // (attn_bwd.hip): M(u) = dV of query tile u-1, then S of tile u; V(u) = P of
-// tile u, its LSE reaching each lane by DPP row broadcast from one 16-byte
-// read of the tile statistics; waves 4..7 one phase behind; Q(u+1), dO^T(u)
+// tile u, its LSE read by row from the tile statistics (four 16-byte LDS
+// broadcast reads per 32-row block); waves 4..7 one phase behind; Q(u+1), dO^T(u)
 // and the statistics of u+1 copied in interval 2u and waited for before
 // barrier 2u+1.
 constexpr uint32_t DV_Q = 0;         // Q row tile at + 16384 * slot
@@ -58,7 +58,10 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) __attribute__((amdgpu_waves_per_e
   for (int s = 0; s < 8; ++s) rf[s] = DV_Q + col * 256 + (((2 * s + half) ^ swz(col)) << 4);
 #pragma unroll
   for (int kg = 0; kg < 4; ++kg) tf[kg] = DV_DOT + col * 128 + (((2 * kg + half) ^ swz8(col)) << 4);
-  const uint32_t sf = DV_ST + 16 * (16 * half + (lane & 15));
+  // LSE log2 e of this lane's rows of value group jg in row block qb: rows
+  // 32 qb + 8 jg + 4 half + 0..3, one 16-byte read shared by the lanes of the
+  // half (an LDS broadcast).
+  const uint32_t sf = DV_ST + 16 * half;
   auto frag = [&](uint32_t off) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8*>(smem + off);
   };
@@ -159,14 +162,18 @@ __global__ __launch_bounds__(64 * DV_WAVES, 1) __attribute__((amdgpu_waves_per_e
       const int t = ks.t0 + u;
       if (late && u + 1 < n) copies(std::integral_constant<int, decltype(parity)::value ^ 1>{}, u + 1);
       if (!KMASK || ks.wave_live) {
-        // {LSE log2 e, -Delta} x 2 row blocks per entry, the tile exponent after the entries
-        const f32x4 st = *reinterpret_cast<const f32x4*>(smem + sf + 1024 * (t & 3));
+        // LSE log2 e of the tile's 64 rows, then -Delta, then the tile exponent
         const int e_q = *reinterpret_cast<const int*>(smem + DV_ST + 1024 * (t & 3) + 512);
         const float g = ldexpf(p.scale_log2, e_q + e_k);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           float l2[16], pv[16];
-          row_bcast16(qb ? st[2] : st[0], l2);
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(smem + sf + 1024 * (t & 3) + 4 * (32 * qb + 8 * jg));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l2[4 * jg + i] = x[i];
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             float pe = __builtin_amdgcn_exp2f(fmaf(s_acc[qb][j], g, -l2[j]));

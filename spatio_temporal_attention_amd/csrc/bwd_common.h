@@ -31,18 +31,6 @@ __device__ __forceinline__ void store_grad4(uint16_t* row_ptr, const RopeDev& ro
   *reinterpret_cast<u32x2*>(row_ptr + d0) = w;
 }
 
-// out[j] = x of lane j of this lane's 16-lane row (DPP row_newbcast:j).
-template <int... J>
-__device__ __forceinline__ void row_bcast16_impl(float x, float* out, std::integer_sequence<int, J...>) {
-  // Every lane is written (the source lane always exists), so no old value is needed.
-  ((out[J] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xf, 0xf,
-                                                                false))),
-   ...);
-}
-__device__ __forceinline__ void row_bcast16(float x, float (&out)[16]) {
-  row_bcast16_impl(x, out, std::make_integer_sequence<int, 16>{});
-}
-
 // Row `r` of a row tile in global memory as the 8 register fragments of the
 // 32x32x16 operand layout (lane half `half` holds chunks 2s + half).
 __device__ __forceinline__ void load_row_frags(bf16x8 (&f)[8], const uint16_t* tile, int r, int half, bool ok) {

@@ -260,19 +260,17 @@ __global__ __launch_bounds__(256) void bwd_q_tiles_kernel(const uint16_t* __rest
   }
   lds_barrier();
   store_t_tile(dot + off, s, tid);
+  // The tile's statistics by row: LSE_i log2 e in floats [0, 64), -Delta_i in
+  // [64, 128), the exponent at 128 (four consecutive rows of one statistic
+  // are one 16-byte read).
   float* st = qstat + (int64_t)blockIdx.x * QSTAT_FLOATS;
-  if (tid < 32) {
-    const int r = 8 * ((tid & 15) >> 2) + 4 * (tid >> 4) + (tid & 3);
-    f32x4 w;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int n = tile * TILE_ROWS + 32 * qb + r;
-      const float x = (n < L) ? lse[((int64_t)b * H + h) * L + n] : -INFINITY;
-      w[2 * qb] = (x > -INFINITY) ? x * 1.4426950408889634f : INFINITY;
-      w[2 * qb + 1] = ndelta_s[32 * qb + r];
-    }
-    *reinterpret_cast<f32x4*>(st + 4 * tid) = w;
-  } else if (tid >= 2 * TILE_ROWS) {
+  if (tid < TILE_ROWS) {
+    const int n = tile * TILE_ROWS + tid;
+    const float x = (n < L) ? lse[((int64_t)b * H + h) * L + n] : -INFINITY;
+    st[tid] = (x > -INFINITY) ? x * 1.4426950408889634f : INFINITY;
+  } else if (tid < 2 * TILE_ROWS) {
+    st[tid] = ndelta_s[tid - TILE_ROWS];
+  } else {
     st[tid] = (tid == 2 * TILE_ROWS) ? __int_as_float(e) : 0.f;
   }
 }
