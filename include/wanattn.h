@@ -267,9 +267,9 @@ int wanattn_lse_merge(const void* const* o_parts, const float* const* lse_parts,
  * Lk, H, D) bytes.  It receives the text keys and values rewritten in 64-key
  * tiles of every (b, h): K as [B, H, ceil(Lk/64), 64, D] bf16 and V
  * transposed as [B, H, ceil(Lk/64), D, 64] bf16, keys past k_lens[b] zero,
- * then 256 bytes the kernel does not use here (the layout is the partial
- * forward's); each part starts on a 256-byte boundary (10.5 MB at Lk = 512,
- * H = 40).  Its contents on return are unspecified.
+ * then a 256-byte work counter (taken from by the workgroups when Lk > 512,
+ * where 8-wave workgroups run); each part starts on a 256-byte boundary
+ * (10.5 MB at Lk = 512, H = 40).  Its contents on return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t wanattn_cross_fwd_workspace_bytes(int B, int Lk, int H, int D);
 

@@ -387,6 +387,7 @@ WANATTN_API int wanattn_cross_fwd(const void* q, const void* k, const void* v, c
   p.Lk = Lk;
   p.H = H;
   p.scale_log2 = scale * LOG2E_F;
+  p.work = (int*)((uint8_t*)ws + wl.work);   // taken by the 8-wave path (more than 8 key tiles)
   return hip_status(launch_attn_fwd_tiled(p, (hipStream_t)stream));
 }
 

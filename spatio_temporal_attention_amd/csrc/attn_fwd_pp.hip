@@ -144,7 +144,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) __attribute__((amdgpu_waves_per_eu
   int n_q = p.Lq;
   if (p.q_lens != nullptr) n_q = min(max(p.q_lens[b], 0), p.Lq);
   const bool row_ok = i < n_q;
-  if (VARLEN && qt * BR >= n_q) return;   // before the first barrier; nothing to compute or store
+  if (VARLEN && qt * BR >= n_q) return;   // uniform over the workgroup; nothing to compute or store
   bf16x8 qf[8];
   float g_q = p.scale_log2;
   {

@@ -3,14 +3,16 @@ from a work counter, at item counts around the spare workgroups.
 
 A launch of n items runs n + ceil(n / 8) workgroups; each takes the counter's
 next value and those past the last item leave at once.  These shapes put n at
-1, 7, 8, 9 and 17 (one 256-row query tile per head), at 8 with a ragged second
-tile per head, and run the partial (ring-hop) forward at 7 items, so the first,
-the last and the spare workgroups all occur; every output row is compared with
-the fp64 oracle at the other parity tests' bar (max-abs 2e-2, rel-L2 5e-3 on
-O; |LSE error| 1e-3)."""
+1, 7, 8, 9 and 17 (one 256-row query tile per head) and at 8 with a ragged
+second tile per head, so the first, the last and the spare workgroups all
+occur; they also run the partial (ring-hop) forward at 7 items and the
+cross-attention forward over 640 text tokens (the 8-wave path, counted).  Every
+output row is compared with the fp64 oracle at the other parity tests' bar
+(max-abs 2e-2, rel-L2 5e-3 on O; |LSE error| 1e-3)."""
 
 import math
 
+import numpy as np
 import pytest
 
 import oracle
@@ -70,5 +72,21 @@ def test_counted_partial_forward_matches_oracle():
     torch.cuda.synchronize()
     ro, rl = oracle.partial_fwd_ref(synth.bf16_bits_to_f64(q), synth.bf16_bits_to_f64(k),
                                     synth.bf16_bits_to_f64(v), SCALE, q_off, k_off, grid, ROPE)
+    check_close("O", bf16_to_f64(o), ro)
+    check_lse("LSE", f32_to_np(lse), rl)
+
+
+def test_counted_cross_forward_long_text():
+    """Cross-attention over 640 text tokens (10 key tiles: the 8-wave path, which takes its query tiles from the
+    counter), 2 items x 3 heads x 2 query tiles (300 rows: the second holds 44), valid lengths 640 and 333."""
+    B, Lq, Lk, H = 2, 300, 640, 3
+    qb = synth.random_bf16(781, (B, Lq, H, 128))
+    kb = synth.random_bf16(782, (B, Lk, H, 128))
+    vb = synth.random_bf16(783, (B, Lk, H, 128))
+    lens = np.array([640, 333], dtype=np.int32)
+    o, lse = wa.cross_fwd(to_dev(qb), to_dev(kb), to_dev(vb), torch.from_numpy(lens).cuda(), scale=SCALE)
+    torch.cuda.synchronize()
+    ro, rl = oracle.cross_fwd_ref(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                                  synth.bf16_bits_to_f64(vb), lens, SCALE)
     check_close("O", bf16_to_f64(o), ro)
     check_lse("LSE", f32_to_np(lse), rl)
