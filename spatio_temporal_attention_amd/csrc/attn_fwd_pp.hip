@@ -35,9 +35,14 @@
 //    run one phase behind waves 0..3 and all eight meet at a barrier after
 //    every phase, so on each SIMD (waves w and w + 4) one wave feeds the
 //    matrix cores while the other runs its softmax;
-//  * workgroups are ordered head-major and XCD-aware (batch item innermost),
-//    so the resident workgroups of one XCD walk the same head's K/V tiles
-//    through its L2.
+//  * the main launches take their query tiles from a work counter in the
+//    workspace, head-major with the batch item innermost: the XCDs of a chip
+//    run at unequal speeds, and the faster ones take more tiles (common.h);
+//    without a counter (the split's own launch) workgroups are ordered
+//    XCD-aware, so the resident workgroups of one XCD walk the same head's
+//    K/V tiles through its L2;
+//  * fixed lengths: the last query tiles run as key ranges at the end of the
+//    main launch, whose fp32 partials a merge pass combines exactly.
 // Built with the iterative ILP machine scheduler (build flags of this file):
 // with the default one the products phase reads each LDS fragment just before
 // its MFMA.
