@@ -234,6 +234,23 @@ def bench_configs(wa, torch, synth, dev, rope, peak_meas, c4_ms):
     return {k: out[k] for k in ("C1", "C2", "C3", "C4", "C5") if k in out}
 
 
+def bench_rope3d(wa, torch, dev, rope):
+    """The standalone 3D RoPE call on the 720p query tensor [1, 75600, 40, 128], out of place: HBM-bound
+    (every element read once and written once, plus the angle table)."""
+    grid, L, H = (21, 45, 80), 75600, 40
+    g = torch.Generator(device=dev).manual_seed(31)
+    x = torch.randn((1, L, H, 128), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    table = wa.rope_table(grid, rope, device=dev)
+    ms = _median_ms(lambda: wa.rope3d(x, grid, table, rope=rope, out=y), reps=50)
+    nbytes = 2.0 * x.numel() * 2 + table.numel() * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del x, y
+    return {"workload": "wanattn_rope3d on q [1, 75600, 40, 128] bf16 (720p grid 21x45x80), out of place",
+            "ms": round(ms, 4), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2)}
+
+
 def bench_cross(wa, torch, dev, g, with_fwd=False):
     """Text cross-attention at the step's shape: 75,600 video tokens over 512 text tokens (336 valid), 40 heads;
     the backward (and with_fwd: the forward) timed on its own."""
@@ -354,7 +371,8 @@ def main():
     if args.configs_only:
         peak = measure_mfma_peak(wa)
         print(json.dumps({"mfma_peak_measured": peak,
-                          "configs": bench_configs(wa, torch, synth, dev, rope, peak["tflops"], None)}), flush=True)
+                          "configs": bench_configs(wa, torch, synth, dev, rope, peak["tflops"], None),
+                          "rope3d": bench_rope3d(wa, torch, dev, rope)}), flush=True)
         return
     w = synth.WORKLOADS[4]
     B, L, H, D = w.B, w.L, w.H, w.D
@@ -484,7 +502,8 @@ def main():
         result["pct_measured_mfma_peak"] = round(100.0 * fwd_tflops / peak["tflops"], 2)
         log(f"MFMA loop: {peak['tflops']} TFLOP/s")
         result["configs"] = bench_configs(wa, torch, synth, dev, rope, peak["tflops"], fwd_med)
-        log("per-config forward timings done")
+        result["rope3d"] = bench_rope3d(wa, torch, dev, rope)
+        log("per-config forward timings and the standalone RoPE done")
     if not args.no_cpu_baseline:
         log("running the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(inp, w, rope, scale)
